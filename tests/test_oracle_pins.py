@@ -1,0 +1,333 @@
+"""Pins for the CPU oracle (run on CPU: ``-m "not gpu"``).
+
+Each test ties one oracle step to something other than its own formula: a
+library routine (NumPy matmul / softmax / Python's sort), a brute force on tiny
+inputs, a closed form, a special case with a known answer, or an invariant.
+They are chosen so that a dropped term, a wrong sign, a wrong index or a
+transposed operand in ``oracle/dsa_oracle.c`` fails at least one of them.
+"""
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+import oracle
+from dsa_top_sparse_amd import synth
+
+
+def _f32(a):
+    return synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
+
+
+# ---------------------------------------------------------------- indexer
+
+
+def _numpy_scores(qidx, w, kidx, offset, ld):
+    """ReLU-weighted head sum through NumPy's float64 matmul, then the causal mask."""
+    q = _f32(qidx).astype(np.float64)
+    k = _f32(kidx).astype(np.float64)
+    n_q = q.shape[0]
+    dots = np.einsum("ihd,jd->ihj", q, k, optimize=True)  # library contraction
+    s = (w.astype(np.float64)[:, :, None] * np.maximum(dots, 0.0)).sum(axis=1)
+    out = np.full((n_q, ld), -np.inf, dtype=np.float32)
+    for i in range(n_q):
+        p = offset + i
+        out[i, : p + 1] = s[i, : p + 1].astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scores_match_numpy_contraction(oracle_lib, dtype):
+    cfg = synth.tiny_config(n_q=37, offset=21, n_idx_heads=3, d_idx=24, idx_dtype=dtype, seed=11)
+    d = synth.generate(cfg)
+    ld = cfg.t_ctx + 5
+    got = oracle.indexer_scores(cfg.n_q, cfg.offset, d["qidx"], d["w"], d["kidx"], ld=ld)
+    ref = _numpy_scores(d["qidx"], d["w"], d["kidx"], cfg.offset, ld)
+    assert np.array_equal(got, ref)
+    assert not np.any(got.view(np.uint32) == 0x80000000)  # no -0.0
+    # every finite score is an exact integer here
+    fin = np.isfinite(got)
+    assert np.array_equal(got[fin], np.round(got[fin]))
+
+
+def test_scores_config_C0_match_numpy(oracle_lib):
+    cfg = synth.CONFIGS["C0"]
+    d = synth.generate(cfg)
+    got = oracle.indexer_scores(cfg.n_q, cfg.offset, d["qidx"], d["w"], d["kidx"])
+    ref = _numpy_scores(d["qidx"], d["w"], d["kidx"], cfg.offset, cfg.t_ctx)
+    assert np.array_equal(got, ref)
+
+
+def test_scores_one_hot_query_picks_key_column(oracle_lib):
+    # Head 1 of query i is the unit vector e_{d_i}; head 0 is zero. Then
+    # s[i][j] = w[i][1] * max(0, kidx[j][d_i]): a transposed operand or a
+    # wrong head index gives other values.
+    rng = np.random.default_rng(5)
+    n_q, off, H, D = 6, 4, 2, 8
+    kidx = rng.integers(-3, 4, size=(off + n_q, D)).astype(np.float32)
+    qidx = np.zeros((n_q, H, D), dtype=np.float32)
+    dsel = rng.integers(0, D, size=n_q)
+    for i in range(n_q):
+        qidx[i, 1, dsel[i]] = 1.0
+    w = np.array([[7.0, 2.0]] * n_q, dtype=np.float32)
+    s = oracle.indexer_scores(n_q, off, qidx, w, kidx)
+    for i in range(n_q):
+        for j in range(off + i + 1):
+            assert s[i, j] == 2.0 * max(0.0, kidx[j, dsel[i]])
+
+
+def test_scores_hand_example(oracle_lib):
+    # Two indexer heads of width 2, one query at position 2 (offset 2).
+    #   q head0 = (1, -2), head1 = (3, 1); w = (1, 2)
+    #   k0 = (1, 1):  head0 dot = -1 -> 0 ; head1 dot = 4 -> 4 ; s = 1*0 + 2*4 = 8
+    #   k1 = (-1, 2): head0 dot = -5 -> 0 ; head1 dot = -1 -> 0 ; s = 0
+    #   k2 = (2, 0):  head0 dot = 2  -> 2 ; head1 dot = 6 -> 6 ; s = 2 + 12 = 14
+    #   k3 is beyond the causal frontier -> -inf
+    qidx = np.array([[[1, -2], [3, 1]]], dtype=np.float32)
+    kidx = np.array([[1, 1], [-1, 2], [2, 0]], dtype=np.float32)
+    w = np.array([[1, 2]], dtype=np.float32)
+    s = oracle.indexer_scores(1, 2, qidx, w, kidx, ld=4)
+    assert s[0].tolist()[:3] == [8.0, 0.0, 14.0] and s[0, 3] == -np.inf
+    # a zero score is +0.0, never -0.0
+    assert s.view(np.uint32)[0, 1] == 0
+
+
+def test_scores_zero_query_gives_positive_zero(oracle_lib):
+    cfg = synth.tiny_config(n_q=9, offset=3, seed=2)
+    d = synth.generate(cfg)
+    q0 = np.zeros_like(d["qidx"]) * -1.0  # -0.0 entries
+    s = oracle.indexer_scores(cfg.n_q, cfg.offset, q0, d["w"], d["kidx"])
+    for i in range(cfg.n_q):
+        row = s[i, : cfg.offset + i + 1]
+        assert np.all(row.view(np.uint32) == 0)
+
+
+def test_scores_causal_boundary_inclusive(oracle_lib):
+    cfg = synth.tiny_config(n_q=5, offset=7, seed=3)
+    d = synth.generate(cfg)
+    ld = cfg.t_ctx + 3
+    s = oracle.indexer_scores(cfg.n_q, cfg.offset, d["qidx"], d["w"], d["kidx"], ld=ld)
+    for i in range(cfg.n_q):
+        p = cfg.offset + i
+        assert np.all(np.isfinite(s[i, : p + 1]))
+        assert np.all(s[i, p + 1:] == -np.inf)
+
+
+def test_scores_absolute_positions_chunk_invariant(oracle_lib):
+    # The same query at the same absolute position gives the same row whether
+    # it is computed in one chunk or in a later chunk with a larger offset.
+    cfg = synth.tiny_config(n_q=40, offset=0, seed=4)
+    d = synth.generate(cfg)
+    whole = oracle.indexer_scores(40, 0, d["qidx"], d["w"], d["kidx"], ld=40)
+    part = oracle.indexer_scores(15, 25, d["qidx"][25:], d["w"][25:], d["kidx"], ld=40)
+    assert np.array_equal(whole[25:], part)
+    sub = oracle.indexer_scores(40, 0, d["qidx"], d["w"], d["kidx"], ld=40, rows=[39, 3, 17])
+    assert np.array_equal(sub, whole[[39, 3, 17]])
+
+
+def test_scores_bf16_widening_exact(oracle_lib):
+    cfg = synth.tiny_config(n_q=12, offset=4, idx_dtype="bf16", seed=8)
+    d = synth.generate(cfg)
+    a = oracle.indexer_scores(cfg.n_q, cfg.offset, d["qidx"], d["w"], d["kidx"])
+    b = oracle.indexer_scores(cfg.n_q, cfg.offset, synth.bf16_bits_to_f32(d["qidx"]), d["w"],
+                              synth.bf16_bits_to_f32(d["kidx"]))
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- top-k
+
+
+def _brute_topk(row, n, k):
+    if n <= k:
+        sel = list(range(n))
+    else:
+        sel = sorted(sorted(range(n), key=lambda j: (-float(row[j]), j))[:k])
+    return sel + [-1] * (k - len(sel))
+
+
+@pytest.mark.parametrize("k", [1, 3, 8, 17])
+def test_topk_python_sort_bruteforce(oracle_lib, k):
+    rng = np.random.default_rng(100 + k)
+    n_q, off = 30, 11
+    scores = rng.integers(0, 5, size=(n_q, off + n_q)).astype(np.float32)  # heavy ties
+    scores[rng.random(scores.shape) < 0.1] *= -1.0  # some -0.0 and negatives
+    for i in range(n_q):
+        scores[i, off + i + 1:] = -np.inf
+    got = oracle.topk_select(n_q, off, k, scores)
+    for i in range(n_q):
+        assert got[i].tolist() == _brute_topk(scores[i], off + i + 1, k), i
+
+
+def test_topk_special_cases(oracle_lib):
+    n_q, off, k = 4, 10, 5
+    ld = off + n_q
+    # all equal -> the k lowest indices
+    s = np.full((n_q, ld), 3.0, dtype=np.float32)
+    assert np.array_equal(oracle.topk_select(n_q, off, k, s), np.tile(np.arange(k), (n_q, 1)))
+    # strictly increasing -> the k highest causal indices
+    s = np.tile(np.arange(ld, dtype=np.float32), (n_q, 1))
+    got = oracle.topk_select(n_q, off, k, s)
+    for i in range(n_q):
+        p = off + i
+        assert got[i].tolist() == list(range(p - k + 1, p + 1))
+    # fewer causal keys than k -> every causal key, then -1 padding
+    got = oracle.topk_select(3, 0, 4, np.zeros((3, 3), dtype=np.float32))
+    assert got.tolist() == [[0, -1, -1, -1], [0, 1, -1, -1], [0, 1, 2, -1]]
+    # -0.0 and +0.0 tie; the lower index wins
+    s = np.array([[1.0, -0.0, 0.0, 2.0]], dtype=np.float32)
+    assert oracle.topk_select(1, 3, 3, s).tolist() == [[0, 1, 3]]
+
+
+@pytest.mark.parametrize("name,stride", [("C0", 1), ("C2", 97), ("C4", 257)])
+def test_topk_properties_on_configs(oracle_lib, name, stride):
+    cfg = synth.CONFIGS[name]
+    d = synth.generate(cfg)
+    rows = list(range(0, cfg.n_q, stride))
+    s = oracle.indexer_scores(cfg.n_q, cfg.offset, d["qidx"], d["w"], d["kidx"], rows=rows)
+    idx = oracle.topk_select(cfg.n_q, cfg.offset, cfg.top_k, s, rows=rows)
+    n_ties_at_threshold = 0
+    for r, i in enumerate(rows):
+        n = cfg.offset + i + 1
+        sel = idx[r][idx[r] >= 0]
+        assert sel.size == min(cfg.top_k, n)
+        assert np.all(np.diff(sel) > 0) and sel.max() < n
+        if n > cfg.top_k:
+            mask = np.zeros(n, dtype=bool)
+            mask[sel] = True
+            row = s[r, :n]
+            thr = row[mask].min()
+            assert row[~mask].max() <= thr
+            tied = np.flatnonzero(row == thr)
+            chosen = tied[mask[tied]]
+            # among tied keys the chosen ones are exactly the lowest indices
+            assert np.array_equal(chosen, tied[: chosen.size])
+            n_ties_at_threshold += int(tied.size > chosen.size)
+    if name != "C0":
+        assert n_ties_at_threshold > 0  # the workloads really exercise the tie rule
+
+
+# ---------------------------------------------------------------- attention
+
+
+def _numpy_attention(q, kv, sel, scale, d_v):
+    """Softmax attention of one query over rows kv[sel] via NumPy float64."""
+    qf = _f32(q).astype(np.float64)
+    k = _f32(kv).astype(np.float64)[sel]
+    logits = scale * (qf @ k.T)  # [H][n]
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ k[:, :d_v], logsumexp(logits, axis=1)
+
+
+def test_attention_dense_causal_identity_C0(oracle_lib):
+    # With top_k >= every causal context, top-k attention is dense causal
+    # attention: softmax(Q K^T * scale + causal mask) V for all rows at once.
+    cfg = synth.CONFIGS["C0"]
+    d = synth.generate(cfg)
+    causal_idx = np.array([[j if j <= i else -1 for j in range(cfg.t_ctx)]
+                           for i in range(cfg.n_q)], dtype=np.int32)
+    out, lse = oracle.sparse_mla(cfg.n_q, 0, cfg.sm_scale, cfg.d_latent, d["q"], d["kv"],
+                                 causal_idx)
+    q = d["q"].astype(np.float64)
+    kv = d["kv"].astype(np.float64)
+    logits = cfg.sm_scale * np.einsum("ihd,jd->hij", q, kv)
+    mask = np.triu(np.ones((cfg.n_q, cfg.t_ctx), dtype=bool), 1)
+    logits[:, mask] = -np.inf
+    p = np.exp(logits - logits.max(axis=2, keepdims=True))
+    p /= p.sum(axis=2, keepdims=True)
+    ref = np.einsum("hij,jc->ihc", p, kv[:, : cfg.d_latent])
+    assert np.max(np.abs(out - ref)) < 1e-12
+    assert np.max(np.abs(lse - logsumexp(logits, axis=2).T)) < 1e-12
+
+
+def test_attention_textbook_reduction_on_selected_rows(oracle_lib):
+    # For rows with more causal keys than k, the oracle equals dense softmax
+    # attention over exactly the gathered rows kv[S_i].
+    cfg = synth.CONFIGS["C2"]
+    d = synth.generate(cfg)
+    rows = [0, 777, 2047]
+    r = oracle.full_path(cfg, d, rows=rows)
+    for t, i in enumerate(rows):
+        sel = r["idx"][t]
+        assert np.all(sel >= 0)
+        ref, ref_lse = _numpy_attention(d["q"][i], d["kv"], sel, cfg.sm_scale, cfg.d_latent)
+        assert np.max(np.abs(r["out"][t] - ref)) < 1e-12
+        assert np.max(np.abs(r["lse"][t] - ref_lse)) < 1e-12
+
+
+def test_attention_single_key_returns_its_value(oracle_lib):
+    cfg = synth.tiny_config(n_q=3, offset=0, seed=21)
+    d = synth.generate(cfg)
+    idx = np.full((1, 4), -1, dtype=np.int32)
+    idx[0, 2] = 0
+    out, lse = oracle.sparse_mla(cfg.n_q, 0, cfg.sm_scale, cfg.d_latent, d["q"], d["kv"], idx,
+                                 rows=[0])
+    assert np.array_equal(out[0], np.tile(d["kv"][0, : cfg.d_latent].astype(np.float64),
+                                          (cfg.n_heads, 1)))
+    exp_lse = cfg.sm_scale * (d["q"][0].astype(np.float64) @ d["kv"][0].astype(np.float64))
+    assert np.max(np.abs(lse[0] - exp_lse)) < 1e-12
+
+
+def test_attention_zero_query_is_mean_of_values(oracle_lib):
+    cfg = synth.tiny_config(n_q=20, offset=30, seed=22)
+    d = synth.generate(cfg)
+    q = np.zeros_like(d["q"])
+    idx = np.array([[3, 9, 40, 12, -1, 0]], dtype=np.int32)
+    out, lse = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, q, d["kv"],
+                                 idx, rows=[15])
+    mean = d["kv"][[3, 9, 40, 12, 0], : cfg.d_latent].astype(np.float64).mean(axis=0)
+    assert np.max(np.abs(out[0] - mean)) < 1e-14
+    assert np.allclose(lse[0], np.log(5.0), atol=1e-14)
+
+
+def test_attention_constant_values_and_two_key_closed_form(oracle_lib):
+    n_q, off, H, dqk, dv = 1, 1, 2, 4, 3
+    kv = np.zeros((2, dqk), dtype=np.float32)
+    kv[:, :dv] = 1.0
+    kv[0, 3], kv[1, 3] = 2.0, -1.0  # key-only (rope) dim drives the logits
+    q = np.zeros((n_q, H, dqk), dtype=np.float32)
+    q[0, 0, 3] = 1.0
+    q[0, 1, 3] = -0.5
+    idx = np.array([[0, 1]], dtype=np.int32)
+    out, lse = oracle.sparse_mla(n_q, off, 1.0, dv, q, kv, idx)
+    assert np.allclose(out, 1.0, atol=1e-15)  # constant values -> weights sum to one
+    # now distinct values: v0 = (1,0,0), v1 = (0,1,0)
+    kv[:, :dv] = 0.0
+    kv[0, 0], kv[1, 1] = 1.0, 1.0
+    out, lse = oracle.sparse_mla(n_q, off, 1.0, dv, q, kv, idx)
+    for h, (l0, l1) in enumerate([(2.0, -1.0), (-1.0, 0.5)]):
+        p0 = 1.0 / (1.0 + np.exp(l1 - l0))
+        assert abs(out[0, h, 0] - p0) < 1e-15 and abs(out[0, h, 1] - (1 - p0)) < 1e-15
+        assert out[0, h, 2] == 0.0
+        assert abs(lse[0, h] - np.logaddexp(l0, l1)) < 1e-14
+
+
+def test_attention_slot_order_padding_and_invalid_slots(oracle_lib):
+    cfg = synth.tiny_config(n_q=10, offset=50, seed=23)
+    d = synth.generate(cfg)
+    base = np.array([[1, 5, 7, 33, 52, 59]], dtype=np.int32)  # query 9 sits at position 59
+    a, la = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, d["q"], d["kv"],
+                              base, rows=[9])
+    perm = np.array([[59, -1, 33, 1, 7, -1, 52, 5, 60, 1000, -7]], dtype=np.int32)
+    b, lb = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, d["q"], d["kv"],
+                              perm, rows=[9])
+    # same multiset of valid keys (60 and 1000 lie beyond position 59, -7 and -1 are not keys)
+    assert np.max(np.abs(a - b)) < 1e-13 and np.max(np.abs(la - lb)) < 1e-13
+    none = np.array([[-1, 60, 61]], dtype=np.int32)
+    c, lc = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, d["q"], d["kv"],
+                              none, rows=[9])
+    assert np.all(c == 0.0) and np.all(lc == -np.inf)
+
+
+def test_attention_bf16_widening_exact(oracle_lib):
+    cfg = synth.tiny_config(n_q=8, offset=8, act_dtype="bf16", seed=24)
+    d = synth.generate(cfg)
+    idx = np.array([[0, 3, 9, 15]], dtype=np.int32)
+    a, _ = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, d["q"], d["kv"],
+                             idx, rows=[7])
+    b, _ = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent,
+                             synth.bf16_bits_to_f32(d["q"]), synth.bf16_bits_to_f32(d["kv"]),
+                             idx, rows=[7])
+    assert np.array_equal(a, b)
+    ref, _ = _numpy_attention(d["q"][7], d["kv"], idx[0], cfg.sm_scale, cfg.d_latent)
+    assert np.max(np.abs(a[0] - ref)) < 1e-13
