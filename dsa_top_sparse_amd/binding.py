@@ -1,0 +1,188 @@
+"""ctypes binding of ``libdsa_amd.so`` (the C ABI in ``include/dsa.h``).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+the library. PyTorch provides device memory and the stream handle. The module
+raises if the library has not been built -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdsa_amd.so")
+
+DSA_BF16 = 0
+DSA_F32 = 1
+
+# Every symbol include/dsa.h declares.
+EXPORTED = (
+    "dsa_indexer_scores",
+    "dsa_topk_workspace_bytes",
+    "dsa_topk_select",
+    "dsa_sparse_mla_fwd",
+    "dsa_status_string",
+    "dsa_version",
+)
+
+STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_DTYPE",
+          -4: "DSA_ERR_UNSUPPORTED", -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_DEVICE",
+          -7: "DSA_ERR_ALIGN"}
+
+
+class Dims(ctypes.Structure):
+    """Mirror of ``dsa_dims``."""
+
+    _fields_ = [
+        ("n_q", ctypes.c_int32),
+        ("offset", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("n_idx_heads", ctypes.c_int32),
+        ("d_idx", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("act_dtype", ctypes.c_int32),
+        ("idx_dtype", ctypes.c_int32),
+    ]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the HIP library (raises if it is missing: build it first)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() "
+                               "(or python -m dsa_top_sparse_amd.build) first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        dp = ctypes.POINTER(Dims)
+        L.dsa_indexer_scores.argtypes = [dp, vp, vp, vp, vp, i64, vp]
+        L.dsa_topk_workspace_bytes.argtypes = [dp]
+        L.dsa_topk_workspace_bytes.restype = sz
+        L.dsa_topk_select.argtypes = [dp, vp, i64, vp, vp, sz, vp]
+        L.dsa_sparse_mla_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd):
+            f.restype = ctypes.c_int
+        L.dsa_status_string.argtypes = [ctypes.c_int]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().dsa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().dsa_version())
+
+
+def make_dims(cfg, n_q: Optional[int] = None, offset: Optional[int] = None) -> Dims:
+    """dsa_dims for a config (anything with the DsaConfig attributes)."""
+    code = {"bf16": DSA_BF16, "f32": DSA_F32}
+    return Dims(cfg.n_q if n_q is None else n_q, cfg.offset if offset is None else offset,
+                cfg.n_heads, cfg.d_latent, cfg.d_rope, cfg.n_idx_heads, cfg.d_idx, cfg.top_k,
+                cfg.sm_scale, code[cfg.act_dtype], code[cfg.idx_dtype])
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DsaError(fn, status)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to the DSA library must be contiguous")
+
+
+def indexer_scores(dims: Dims, q_idx, w_idx, k_idx, scores, ld: int, stream=None) -> None:
+    _contig(q_idx, w_idx, k_idx, scores)
+    _check("dsa_indexer_scores", lib().dsa_indexer_scores(
+        ctypes.byref(dims), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(scores), int(ld),
+        _stream(stream)))
+
+
+def topk_workspace_bytes(dims: Dims) -> int:
+    return int(lib().dsa_topk_workspace_bytes(ctypes.byref(dims)))
+
+
+def topk_select(dims: Dims, scores, ld: int, idx, workspace=None, stream=None) -> None:
+    _contig(scores, idx)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_topk_select", lib().dsa_topk_select(
+        ctypes.byref(dims), _ptr(scores), int(ld), _ptr(idx), _ptr(workspace), ws,
+        _stream(stream)))
+
+
+def sparse_mla_fwd(dims: Dims, q, kv, idx, out, lse=None, stream=None) -> None:
+    _contig(q, kv, idx, out, lse)
+    _check("dsa_sparse_mla_fwd", lib().dsa_sparse_mla_fwd(
+        ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
+# ---------------------------------------------------------------- plumbing
+
+
+def to_device(inputs: Dict, device="cuda") -> Dict:
+    """Host arrays from the seeded generator -> device tensors (bf16 stays bf16 bits)."""
+    import numpy as np
+    import torch
+    out = {}
+    for k, v in inputs.items():
+        if not isinstance(v, np.ndarray) or k.startswith("dup_"):
+            continue
+        if v.dtype == np.uint16:
+            t = torch.from_numpy(v.view(np.int16)).to(device).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+        out[k] = t
+    return out
+
+
+def alloc_outputs(cfg, device="cuda", ld: Optional[int] = None, with_lse: bool = True) -> Dict:
+    import torch
+    ld = cfg.t_ctx if ld is None else ld
+    o = {
+        "scores": torch.empty((cfg.n_q, ld), dtype=torch.float32, device=device),
+        "idx": torch.empty((cfg.n_q, cfg.top_k), dtype=torch.int32, device=device),
+        "out": torch.empty((cfg.n_q, cfg.n_heads, cfg.d_latent), dtype=torch.float32, device=device),
+        "lse": torch.empty((cfg.n_q, cfg.n_heads), dtype=torch.float32, device=device) if with_lse else None,
+        "ld": ld,
+    }
+    ws = topk_workspace_bytes(make_dims(cfg))
+    o["workspace"] = torch.empty(ws, dtype=torch.uint8, device=device) if ws else None
+    return o
+
+
+def run_chunk(cfg, dev: Dict, outs: Dict, stream=None) -> None:
+    """The whole hot path for one chunk: indexer -> top-k -> sparse attention."""
+    dims = make_dims(cfg)
+    indexer_scores(dims, dev["qidx"], dev["w"], dev["kidx"], outs["scores"], outs["ld"], stream)
+    topk_select(dims, outs["scores"], outs["ld"], outs["idx"], outs["workspace"], stream)
+    sparse_mla_fwd(dims, dev["q"], dev["kv"], outs["idx"], outs["out"], outs["lse"], stream)

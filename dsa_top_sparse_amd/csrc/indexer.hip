@@ -1,0 +1,217 @@
+// indexer.hip -- step 1 of the DSA prefill path: indexer scores.
+//
+// For query i (absolute position p = offset + i) and key j:
+//   s[i][j] = sum_h w[i][h] * max(0, <q_idx[i][h], k_idx[j]>)   for j <= p,
+//   s[i][j] = -inf                                               for p < j < ld.
+// (feedman.me page, per-component profile row "DSA indexer"; the formula is
+// this library's reading, the pages print none.)
+//
+// Fast kernel (bf16, 4 indexer heads): one dense contraction on the matrix
+// cores. Rows of the A operand are (query, head) pairs laid out as 4*q + h, so
+// in the 32x32 MFMA result each lane holds the 4 head dot products of one
+// (query, key) pair and the ReLU / weight / head sum happens in registers.
+// Each lane then stores one fp32 score; 32 lanes cover 32 consecutive keys of
+// one query row (128-byte segments).
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kIdxThreads = 256;   // 4 waves
+constexpr int kIdxQueries = 64;    // queries per workgroup (16 per wave)
+constexpr int kIdxHeads = 4;
+
+__device__ __forceinline__ float plain_load(const float* p, int64_t e) { return p[e]; }
+__device__ __forceinline__ float plain_load(const uint16_t* p, int64_t e) { return bf16_to_f32(p[e]); }
+
+// Any dtype / head count / width. grid = (ceil(ld / 256), n_q).
+template <typename T>
+__global__ __launch_bounds__(256) void indexer_plain_kernel(int n_q, int offset, int n_heads,
+                                                            int d_idx, const T* __restrict__ q_idx,
+                                                            const float* __restrict__ w,
+                                                            const T* __restrict__ k_idx,
+                                                            float* __restrict__ scores, int64_t ld) {
+  extern __shared__ float sq[];  // [n_heads][d_idx] of this query
+  const int i = blockIdx.y;
+  const int hd = n_heads * d_idx;
+  for (int e = threadIdx.x; e < hd; e += blockDim.x) sq[e] = plain_load(q_idx, (int64_t)i * hd + e);
+  __syncthreads();
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= ld) return;
+  const int64_t p = (int64_t)offset + i;
+  float out = -INFINITY;
+  if (j <= p) {
+    float s = 0.0f;
+    for (int h = 0; h < n_heads; ++h) {
+      float dot = 0.0f;
+      for (int d = 0; d < d_idx; ++d) dot = fmaf(sq[h * d_idx + d], plain_load(k_idx, j * d_idx + d), dot);
+      s = fmaf(w[(int64_t)i * n_heads + h], fmaxf(dot, 0.0f), s);
+    }
+    out = (s == 0.0f) ? 0.0f : s;  // +0.0, never -0.0
+  }
+  scores[(int64_t)i * ld + j] = out;
+}
+
+// Fill scores[rows q0 .. q0+nrows)[k0 .. k1) with -inf (fully non-causal range).
+__device__ __forceinline__ void fill_neg_inf(float* __restrict__ scores, int64_t ld, int q0, int nrows,
+                                             int64_t k0, int64_t k1) {
+  const int width = (int)(k1 - k0);
+  for (int r = 0; r < nrows; ++r) {
+    float* row = scores + (int64_t)(q0 + r) * ld + k0;
+    for (int c = threadIdx.x; c < width; c += kIdxThreads) __builtin_nontemporal_store(-INFINITY, row + c);
+  }
+}
+
+// bf16, 4 indexer heads, d_idx = D (multiple of 16).
+// Work unit = (64-query block, range of `keys_per_unit` keys). Units are laid
+// out so that the units one XCD runs share a key range: workgroups are handed
+// to the 8 XCDs round-robin, so unit u = xcd * units_per_xcd + slot keeps the
+// indexer keys of one range hot in that XCD's L2 while the queries stream.
+template <int D>
+__global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
+    int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
+    int n_units, int units_per_xcd, int keys_per_unit) {
+  constexpr int KS = D / 16;  // k-steps of the 32x32x16 MFMA
+  const int bid = blockIdx.x;
+  const int u = (bid & 7) * units_per_xcd + (bid >> 3);
+  if (u >= n_units) return;
+  const int kr = u / n_qb;
+  const int qb = u - kr * n_qb;
+  const int q0 = qb * kIdxQueries;
+  const int nrows = min(kIdxQueries, n_q - q0);
+  const int64_t k_begin = (int64_t)kr * keys_per_unit;
+  const int64_t k_end = min<int64_t>(ld, k_begin + keys_per_unit);
+  const int64_t t_ctx = (int64_t)offset + n_q;
+  const int64_t p_max = (int64_t)offset + q0 + nrows - 1;
+  if (k_begin > p_max) {  // every key of the range lies beyond every query of the block
+    fill_neg_inf(scores, ld, q0, nrows, k_begin, k_end);
+    return;
+  }
+
+  __shared__ float sw[kIdxQueries][kIdxHeads];
+  for (int e = threadIdx.x; e < kIdxQueries * kIdxHeads; e += kIdxThreads) {
+    const int q = e >> 2;
+    sw[q][e & 3] = (q < nrows) ? w[(int64_t)(q0 + q) * kIdxHeads + (e & 3)] : 0.0f;
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // A operand: rows (query, head) = 4*q + h of this wave's 16 queries, two
+  // 32-row blocks. Lane holds row l32, k-slice 8*hi .. 8*hi+7 of each k-step.
+  bf16x8 a[2][KS];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int qrow = wave * 16 + mb * 8 + (l32 >> 2);  // query within the block
+    const bool ok = qrow < nrows;
+    const uint16_t* src = q_idx + ((int64_t)(q0 + (ok ? qrow : 0)) * kIdxHeads + (l32 & 3)) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = ok ? *reinterpret_cast<const u32x4*>(src + 16 * ks) : u32x4{0, 0, 0, 0};
+      a[mb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  __syncthreads();
+
+  for (int64_t nb = k_begin; nb < k_end; nb += 32) {
+    const int64_t key = nb + l32;
+    if (nb > p_max) {  // whole 32-key block is beyond the causal frontier
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qrow = wave * 16 + mb * 8 + 2 * g + hi;
+          if (qrow < nrows && key < k_end)
+            __builtin_nontemporal_store(-INFINITY, scores + (int64_t)(q0 + qrow) * ld + key);
+        }
+      continue;
+    }
+    // B operand: key row (clamped into the cache; clamped keys are masked).
+    const int64_t krow = key < t_ctx ? key : t_ctx - 1;
+    const uint16_t* bsrc = k_idx + krow * D + 8 * hi;
+    bf16x8 b[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bsrc + 16 * ks));
+    f32x16 acc[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      acc[mb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][ks], b[ks], acc[mb], 0, 0, 0);
+    }
+    // Result layout: register r of lane (l32, hi) holds row 8*(r/4) + 4*hi + r%4
+    // = 4*query + head with query = 2*(r/4) + hi and head = r%4, column l32.
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qrow = wave * 16 + mb * 8 + 2 * g + hi;
+        if (qrow < nrows && key < k_end) {
+          float s = 0.0f;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) s = fmaf(sw[qrow][h], fmaxf(acc[mb][4 * g + h], 0.0f), s);
+          s = (s == 0.0f) ? 0.0f : s;
+          const int64_t p = (int64_t)offset + q0 + qrow;
+          __builtin_nontemporal_store(key <= p ? s : -INFINITY, scores + (int64_t)(q0 + qrow) * ld + key);
+        }
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_mfma(const IndexerArgs& a, hipStream_t s) {
+  const int n_qb = (a.n_q + kIdxQueries - 1) / kIdxQueries;
+  // Aim for >= 2048 workgroups (8 per CU) with 32-key-aligned ranges.
+  int64_t target_ranges = (2048 + n_qb - 1) / n_qb;
+  int64_t kpu = (a.ld + target_ranges - 1) / target_ranges;
+  kpu = ((kpu + 31) / 32) * 32;
+  if (kpu < 128) kpu = 128;
+  if (kpu > 1024) kpu = 1024;
+  const int64_t n_kr = (a.ld + kpu - 1) / kpu;
+  const int64_t n_units = n_kr * n_qb;
+  if (n_units > (int64_t)1 << 30) return hipErrorInvalidValue;
+  const int units_per_xcd = (int)((n_units + 7) / 8);
+  const int grid = units_per_xcd * 8;
+  hipLaunchKernelGGL(indexer_mfma_kernel<D>, dim3(grid), dim3(kIdxThreads), 0, s, a.n_q, a.offset,
+                     static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx),
+                     a.scores, a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexer_fast_path(const IndexerArgs& a) {
+  return a.bf16 && a.n_idx_heads == kIdxHeads &&
+         (a.d_idx == 32 || a.d_idx == 64 || a.d_idx == 128 || a.d_idx == 256);
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  if (indexer_fast_path(a)) {
+    switch (a.d_idx) {
+      case 32: return launch_mfma<32>(a, s);
+      case 64: return launch_mfma<64>(a, s);
+      case 128: return launch_mfma<128>(a, s);
+      case 256: return launch_mfma<256>(a, s);
+    }
+  }
+  const int64_t gx = (a.ld + 255) / 256;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  const size_t lds = sizeof(float) * (size_t)a.n_idx_heads * a.d_idx;
+  if (a.bf16)
+    hipLaunchKernelGGL(indexer_plain_kernel<uint16_t>, dim3((unsigned)gx, a.n_q), dim3(256), lds, s, a.n_q,
+                       a.offset, a.n_idx_heads, a.d_idx, static_cast<const uint16_t*>(a.q_idx), a.w,
+                       static_cast<const uint16_t*>(a.k_idx), a.scores, a.ld);
+  else
+    hipLaunchKernelGGL(indexer_plain_kernel<float>, dim3((unsigned)gx, a.n_q), dim3(256), lds, s, a.n_q,
+                       a.offset, a.n_idx_heads, a.d_idx, static_cast<const float*>(a.q_idx), a.w,
+                       static_cast<const float*>(a.k_idx), a.scores, a.ld);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,307 @@
+// topk.hip -- step 2 of the DSA prefill path: per-query top-k selection.
+//
+// For query i (absolute position p = offset + i) the causal scores are
+// scores[i][0 .. p]. If p + 1 <= k every causal key is kept; otherwise the k
+// keys first in (score descending, key index ascending) order are kept. The
+// kept indices are written ascending, padded with -1 to k. (feedman.me page:
+// "the per-query top-2048 gather kernel"; the tie rule is this library's
+// contract: a tie at the threshold goes to the lower key index.)
+//
+// One workgroup per query row, an exact radix select on the order-preserving
+// uint32 image of each score (12 + 10 + 10 bits):
+//   pass 1  (HBM): 4096-bin histogram of the top 12 bits in LDS
+//                  -> bucket b1 holding the k-th largest key;
+//   pass 2  (L2) : if the keys with top bits >= b1 fit in LDS, compact them
+//                  (key, index) into LDS in index order (wave ballots +
+//                  a block scan), so every later pass runs out of LDS;
+//   refine       : 1024-bin histograms of the next 10 and last 10 bits among
+//                  the keys of the boundary bucket -> exact threshold T and
+//                  r = number of keys equal to T that still fit;
+//   emit         : in index order, keep key > T, and key == T while fewer
+//                  than r ties have been kept; the output position of a kept
+//                  key is (#greater before it) + min(#ties before it, r).
+// If the candidates do not fit in LDS, the refine and emit passes re-read the
+// row from global memory instead (same arithmetic).
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kTkThreads = 512;
+constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kSlice = 4 * kTkThreads;  // elements per block-wide step (4 per thread)
+constexpr int kBins1 = 4096;            // top 12 bits
+constexpr int kBins2 = 1024;            // 10 bits
+constexpr int kTkCap = 6144;            // LDS candidate capacity
+
+struct TopkSmem {
+  uint32_t hist[kBins1];
+  uint32_t ckey[kTkCap];
+  int32_t cidx[kTkCap];
+  uint64_t scan[2][kTkWaves];
+  uint32_t bc[4];
+};
+
+// Block-wide exclusive scan of a uint64 (callers pack independent counters in
+// bit fields that cannot overflow into each other). `buf` alternates between
+// calls so that a single barrier per scan suffices.
+__device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* total, TopkSmem& sm, int& buf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t lo = __shfl_up(static_cast<uint32_t>(x), o);
+    const uint32_t hi = __shfl_up(static_cast<uint32_t>(x >> 32), o);
+    if (lane >= o) x += (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+  if (lane == kWave - 1) sm.scan[buf][wave] = x;
+  __syncthreads();
+  uint64_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTkWaves; ++w) {
+    const uint64_t t = sm.scan[buf][w];
+    before += (w < wave) ? t : 0;
+    all += t;
+  }
+  buf ^= 1;
+  *total = all;
+  return before + x - v;
+}
+
+// Finds the bucket b (scanning from the top bin down) at which the running
+// count of keys reaches `need`; returns b and the count strictly above it.
+// Requires that the histogram holds at least `need` keys.
+__device__ __forceinline__ void select_bucket(TopkSmem& sm, int nbins, uint32_t need, uint32_t* b_out,
+                                              uint32_t* above_out, uint32_t* cnt_out, int& buf) {
+  const int per = nbins / kTkThreads;
+  const int lo = threadIdx.x * per;
+  uint32_t local = 0;
+  for (int b = 0; b < per; ++b) local += sm.hist[lo + b];
+  uint64_t total;
+  const uint64_t excl = block_excl_scan(local, &total, sm, buf);
+  const uint32_t above = static_cast<uint32_t>(total - excl - local);  // keys in higher bins
+  if (above < need && above + local >= need) {
+    uint32_t run = above;
+    for (int b = lo + per - 1; b >= lo; --b) {
+      const uint32_t h = sm.hist[b];
+      if (run + h >= need) {
+        sm.bc[0] = b;
+        sm.bc[1] = run;
+        sm.bc[2] = h;
+        break;
+      }
+      run += h;
+    }
+  }
+  __syncthreads();
+  *b_out = sm.bc[0];
+  *above_out = sm.bc[1];
+  *cnt_out = sm.bc[2];
+}
+
+// Loads elements base + 4*tid + e (e < 4) of the row; lanes past n get -inf.
+template <bool ALIGNED>
+__device__ __forceinline__ f32x4 load4(const float* __restrict__ row, int base, int n) {
+  const int j = base + 4 * threadIdx.x;
+  f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (ALIGNED) {
+    if (j < n) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + j));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (j + e < n) v[e] = row[j + e];
+  }
+  return v;
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, const float* __restrict__ scores,
+                                                          int64_t ld, int32_t* __restrict__ idx) {
+  __shared__ TopkSmem sm;
+  int buf = 0;
+  const int i = blockIdx.x;
+  const int n = offset + i + 1;  // causal keys 0 .. p (fits int32: validated on the host)
+  int32_t* __restrict__ out = idx + static_cast<int64_t>(i) * k;
+  if (n <= k) {
+    for (int t = threadIdx.x; t < k; t += kTkThreads) out[t] = t < n ? t : -1;
+    return;
+  }
+  const float* __restrict__ row = scores + static_cast<int64_t>(i) * ld;
+  const int tid = threadIdx.x;
+
+  // ---- pass 1: histogram of the top 12 bits over the causal prefix.
+  for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 4 * kSlice) {
+    f32x4 v[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] = load4<ALIGNED>(row, base + s * kSlice, n);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (base + s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[score_key(v[s][e]) >> 20], 1u);
+  }
+  __syncthreads();
+  uint32_t b1, above1, cnt1;
+  select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
+  const bool in_lds = above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
+
+  // ---- pass 2: ordered compaction of every key with top bits >= b1 into LDS.
+  if (in_lds) {
+    uint32_t cbase = 0;
+    for (int base = 0; base < n; base += 4 * kSlice) {
+      f32x4 v[4];
+      uint32_t key[4][4];
+      uint64_t packed = 0;  // 4 x 16-bit per-slice counts (each slice total <= 2048)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        v[s] = load4<ALIGNED>(row, base + s * kSlice, n);
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          key[s][e] = score_key(v[s][e]);
+          const bool f = (base + s * kSlice + 4 * tid + e < n) && (key[s][e] >> 20) >= b1;
+          c += f;
+        }
+        packed |= static_cast<uint64_t>(c) << (16 * s);
+      }
+      uint64_t tot;
+      const uint64_t excl = block_excl_scan(packed, &tot, sm, buf);
+      uint32_t slice_base = cbase;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t pos = slice_base + static_cast<uint32_t>((excl >> (16 * s)) & 0xFFFF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = base + s * kSlice + 4 * tid + e;
+          if (j < n && (key[s][e] >> 20) >= b1 && pos < static_cast<uint32_t>(kTkCap)) {
+            sm.ckey[pos] = key[s][e];
+            sm.cidx[pos] = j;
+            ++pos;
+          }
+        }
+        slice_base += static_cast<uint32_t>((tot >> (16 * s)) & 0xFFFF);
+      }
+      cbase = slice_base;
+    }
+    __syncthreads();
+  }
+  const int n_cand = static_cast<int>(above1 + cnt1);
+
+  // ---- refine: exact threshold inside bucket b1 with two 10-bit digits.
+  uint32_t need = static_cast<uint32_t>(k) - above1;
+  uint32_t prefix = b1;  // decided top bits, right-aligned
+  int shift = 20;        // number of undecided low bits
+  uint32_t tie_cnt = cnt1;
+  for (int level = 0; level < 2 && tie_cnt != need; ++level) {
+    for (int b = tid; b < kBins2; b += kTkThreads) sm.hist[b] = 0;
+    __syncthreads();
+    const int nshift = shift - 10;
+    if (in_lds) {
+      for (int c = tid; c < n_cand; c += kTkThreads) {
+        const uint32_t key = sm.ckey[c];
+        if ((key >> shift) == prefix) atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
+      }
+    } else {
+      for (int base = 0; base < n; base += kSlice) {
+        const f32x4 v = load4<ALIGNED>(row, base, n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = score_key(v[e]);
+          if (base + 4 * tid + e < n && (key >> shift) == prefix) atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    uint32_t b, above, cnt;
+    select_bucket(sm, kBins2, need, &b, &above, &cnt, buf);
+    need -= above;
+    prefix = (prefix << 10) | b;
+    shift = nshift;
+    tie_cnt = cnt;
+  }
+  // Keys with (key >> shift) > prefix are kept; of those equal, the first `need`.
+  const uint32_t r = need;
+
+  // ---- emit in index order.
+  uint32_t gt_base = 0, tie_base = 0;
+  if (in_lds) {
+    for (int base = 0; base < n_cand; base += kSlice) {
+      uint32_t gt[4], tie[4];
+      int32_t jj[4];
+      uint32_t cgt = 0, ctie = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = base + 4 * tid + e;
+        const bool valid = c < n_cand;
+        const uint32_t key = valid ? sm.ckey[c] : 0u;
+        jj[e] = valid ? sm.cidx[c] : -1;
+        gt[e] = valid && (key >> shift) > prefix;
+        tie[e] = valid && (key >> shift) == prefix;
+        cgt += gt[e];
+        ctie += tie[e];
+      }
+      uint64_t tot;
+      const uint64_t excl = block_excl_scan((static_cast<uint64_t>(ctie) << 32) | cgt, &tot, sm, buf);
+      uint32_t g = gt_base + static_cast<uint32_t>(excl);
+      uint32_t t = tie_base + static_cast<uint32_t>(excl >> 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pos = gt[e] ? g + min(t, r) : g + t;  // < k by construction
+        if ((gt[e] || (tie[e] && t < r)) && pos < static_cast<uint32_t>(k)) out[pos] = jj[e];
+        g += gt[e];
+        t += tie[e];
+      }
+      gt_base += static_cast<uint32_t>(tot);
+      tie_base += static_cast<uint32_t>(tot >> 32);
+    }
+  } else {
+    for (int base = 0; base < n; base += kSlice) {
+      const f32x4 v = load4<ALIGNED>(row, base, n);
+      uint32_t gt[4], tie[4];
+      uint32_t cgt = 0, ctie = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = base + 4 * tid + e < n;
+        const uint32_t key = score_key(v[e]);
+        gt[e] = valid && (key >> shift) > prefix;
+        tie[e] = valid && (key >> shift) == prefix;
+        cgt += gt[e];
+        ctie += tie[e];
+      }
+      uint64_t tot;
+      const uint64_t excl = block_excl_scan((static_cast<uint64_t>(ctie) << 32) | cgt, &tot, sm, buf);
+      uint32_t g = gt_base + static_cast<uint32_t>(excl);
+      uint32_t t = tie_base + static_cast<uint32_t>(excl >> 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = base + 4 * tid + e;
+        const uint32_t pos = gt[e] ? g + min(t, r) : g + t;  // < k by construction
+        if ((gt[e] || (tie[e] && t < r)) && pos < static_cast<uint32_t>(k)) out[pos] = j;
+        g += gt[e];
+        t += tie[e];
+      }
+      gt_base += static_cast<uint32_t>(tot);
+      tie_base += static_cast<uint32_t>(tot >> 32);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  const bool aligned = (a.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
+  if (aligned)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores,
+                       a.ld, a.idx);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores,
+                       a.ld, a.idx);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from dsa_top_sparse_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, DEV, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 1 << 20  # an aligned address that is never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def dims(**kw):
+    base = dict(n_q=16, offset=100, n_heads=64, d_latent=512, d_rope=64, n_idx_heads=4, d_idx=128,
+                top_k=2048, sm_scale=1.0 / 24.0, act_dtype=0, idx_dtype=0)
+    base.update(kw)
+    return binding.Dims(*[base[f] for f, _ in binding.Dims._fields_])
+
+
+def test_exports_every_declared_symbol(L):
+    decl = declared_functions()
+    assert decl == sorted(binding.EXPORTED)
+    for name in decl:
+        assert hasattr(L, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                        check=True).stdout
+    exported = sorted(set(re.findall(r" T (dsa_[a-z0-9_]+)$", nm, flags=re.M)))
+    assert exported == decl
+    # nothing but the C ABI is exported
+    assert not re.search(r" T _Z", nm)
+
+
+def test_status_strings_and_version(L):
+    for s in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, DEV, ALIGN):
+        assert binding.status_string(s) and binding.status_string(s) != "unknown status"
+    assert binding.status_string(12345) == "unknown status"
+    assert binding.version() >= 100
+
+
+def test_dims_struct_layout_matches_header():
+    # 8 int32 + float + 2 int32, no padding
+    assert ctypes.sizeof(binding.Dims) == 11 * 4
+
+
+def _idx(L, d, ld=None, p=(FAKE, FAKE, FAKE, FAKE)):
+    ld = d.offset + d.n_q if ld is None else ld
+    return L.dsa_indexer_scores(ctypes.byref(d), p[0], p[1], p[2], p[3], ld, None)
+
+
+def test_indexer_rejects_bad_arguments(L):
+    assert L.dsa_indexer_scores(None, FAKE, FAKE, FAKE, FAKE, 200, None) == NULL
+    assert _idx(L, dims(n_q=-1)) == SHAPE
+    assert _idx(L, dims(offset=-5)) == SHAPE
+    assert _idx(L, dims(offset=2**31 - 10, n_q=20), ld=2**31 + 10) == SHAPE
+    assert _idx(L, dims(n_idx_heads=0)) == SHAPE
+    assert _idx(L, dims(d_idx=-1)) == SHAPE
+    assert _idx(L, dims(idx_dtype=7)) == DTYPE
+    assert _idx(L, dims(), ld=115) == SHAPE  # ld < offset + n_q
+    assert _idx(L, dims(), p=(FAKE, None, FAKE, FAKE)) == NULL
+    assert _idx(L, dims(), p=(FAKE, FAKE, FAKE, FAKE + 4)) == ALIGN
+    # plain-kernel limit: n_idx_heads * d_idx above the LDS-resident row
+    assert _idx(L, dims(n_idx_heads=3, d_idx=4096)) == UNSUP
+    # an empty chunk is a no-op, pointers may be NULL
+    assert _idx(L, dims(n_q=0), ld=100, p=(None, None, None, None)) == OK
+
+
+def test_topk_rejects_bad_arguments(L):
+    d = dims()
+    ld = d.offset + d.n_q
+    assert L.dsa_topk_workspace_bytes(ctypes.byref(d)) == 0
+    assert L.dsa_topk_select(None, FAKE, ld, FAKE, None, 0, None) == NULL
+    assert L.dsa_topk_select(ctypes.byref(dims(top_k=0)), FAKE, ld, FAKE, None, 0, None) == SHAPE
+    assert L.dsa_topk_select(ctypes.byref(dims(top_k=(1 << 20) + 1)), FAKE, ld, FAKE, None, 0, None) == SHAPE
+    assert L.dsa_topk_select(ctypes.byref(d), FAKE, ld - 1, FAKE, None, 0, None) == SHAPE
+    assert L.dsa_topk_select(ctypes.byref(d), None, ld, FAKE, None, 0, None) == NULL
+    assert L.dsa_topk_select(ctypes.byref(d), FAKE, ld, FAKE + 8, None, 0, None) == ALIGN
+    assert L.dsa_topk_select(ctypes.byref(dims(n_q=0)), None, 100, None, None, 0, None) == OK
+
+
+def test_attention_rejects_bad_arguments(L):
+    def call(d, q=FAKE, kv=FAKE, idx=FAKE, out=FAKE, lse=None):
+        return L.dsa_sparse_mla_fwd(ctypes.byref(d), q, kv, idx, out, lse, None)
+
+    assert L.dsa_sparse_mla_fwd(None, FAKE, FAKE, FAKE, FAKE, None, None) == NULL
+    assert call(dims(n_heads=0)) == SHAPE
+    assert call(dims(d_latent=0)) == SHAPE
+    assert call(dims(d_rope=-1)) == SHAPE
+    assert call(dims(top_k=0)) == SHAPE
+    assert call(dims(sm_scale=float("nan"))) == SHAPE
+    assert call(dims(sm_scale=float("inf"))) == SHAPE
+    assert call(dims(act_dtype=2)) == DTYPE
+    assert call(dims(), kv=None) == NULL
+    assert call(dims(), out=None) == NULL
+    assert call(dims(), lse=FAKE + 4) == ALIGN
+    # plain-kernel limits: wide rows or very large k
+    assert call(dims(n_heads=8, d_latent=4000, d_rope=64)) == UNSUP
+    assert call(dims(n_heads=8, top_k=5000)) == UNSUP
+    assert call(dims(n_q=0), q=None, kv=None, idx=None, out=None) == OK

@@ -1,0 +1,271 @@
+"""GPU parity of the HIP path against the CPU oracle (``-m gpu``, MI355X).
+
+Every case calls the library through its C ABI (``dsa_top_sparse_amd.binding``)
+on seeded synthetic inputs and compares with ``oracle``:
+  * indexer scores and top-k indices: bit-exact on sampled query rows (all
+    rows for the small configs), plus the selection properties on every row;
+  * attention: max |out - ref| <= 4e-3, relative L2 <= 5e-3, |lse - ref| <= 1e-3
+    on the sampled rows (the fp64 oracle is too slow for every row at 8k x 2k).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from dsa_top_sparse_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 4e-3
+RTOL_L2 = 5e-3
+LSE_ATOL = 1e-3
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    binding.lib()  # fails loudly when the HIP library is missing
+    oracle.build(force=False)
+    return torch
+
+
+def sample_rows(n_q, seed, extra=24):
+    fixed = [0, 1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 511, 512, 513, 1000, n_q // 2,
+             n_q - 2, n_q - 1]
+    rng = np.random.default_rng(1000 + seed)
+    rnd = rng.choice(n_q, size=min(extra, n_q), replace=False).tolist()
+    return sorted({r for r in fixed + rnd if 0 <= r < n_q})
+
+
+def run_gpu(torch, cfg, inputs, ld=None, with_lse=True):
+    dev = binding.to_device(inputs)
+    outs = binding.alloc_outputs(cfg, ld=ld, with_lse=with_lse)
+    binding.run_chunk(cfg, dev, outs)
+    torch.cuda.synchronize()
+    return dev, outs
+
+
+def check_attention(got_out, got_lse, ref_out, ref_lse, label):
+    diff = np.abs(got_out.astype(np.float64) - ref_out)
+    max_abs = float(diff.max()) if diff.size else 0.0
+    rel = float(np.linalg.norm(got_out.astype(np.float64) - ref_out) / max(np.linalg.norm(ref_out), 1e-300))
+    _say(f"{label}: attention max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert max_abs <= ATOL, f"{label}: max abs err {max_abs}"
+    assert rel <= RTOL_L2, f"{label}: rel L2 {rel}"
+    if got_lse is not None:
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(got_lse), fin)
+        if fin.any():
+            lerr = float(np.abs(got_lse[fin] - ref_lse[fin]).max())
+            assert lerr <= LSE_ATOL, f"{label}: lse err {lerr}"
+
+
+def check_topk_properties(torch, scores, idx, offset, k, label):
+    """Selection properties on every row, using the GPU's own (verified) scores."""
+    n_q = idx.shape[0]
+    pos = torch.arange(n_q, device=idx.device, dtype=torch.int64) + offset
+    n = pos + 1
+    valid = idx >= 0
+    cnt = valid.sum(1)
+    assert torch.equal(cnt, torch.clamp(n, max=k)), f"{label}: wrong selected count"
+    # ascending, in range, no duplicates
+    sel = torch.where(valid, idx.long(), torch.full_like(idx.long(), -1))
+    d = sel[:, 1:] - sel[:, :-1]
+    both = valid[:, 1:] & valid[:, :-1]
+    assert bool(((d > 0) | ~both).all()), f"{label}: not strictly ascending"
+    assert bool((sel.max(1).values <= pos).all()), f"{label}: non-causal index"
+    # valid slots form a prefix (padding at the tail only)
+    assert bool((valid[:, 1:] <= valid[:, :-1]).all())
+    rows = torch.nonzero(n > k).flatten()
+    if rows.numel() == 0:
+        return
+    chunk = 256
+    for r0 in range(0, rows.numel(), chunk):
+        rr = rows[r0:r0 + chunk]
+        S = scores[rr]  # [R][ld]
+        sel_idx = idx[rr].long()
+        sel_s = torch.gather(S, 1, sel_idx)
+        thr = sel_s.min(1).values  # k-th largest
+        col = torch.arange(S.shape[1], device=S.device)
+        causal = col[None, :] <= pos[rr][:, None]
+        greater = ((S > thr[:, None]) & causal).sum(1)
+        assert bool((greater <= k).all()), f"{label}: a larger score was left out"
+        # ties at the threshold: the kept ones are the lowest indices
+        eq = (S == thr[:, None]) & causal
+        n_eq_kept = (sel_s == thr[:, None]).sum(1)
+        rank = torch.cumsum(eq.int(), 1)  # 1-based rank among ties
+        mark = torch.zeros_like(S, dtype=torch.bool)
+        mark.scatter_(1, sel_idx, True)
+        kept_tie = eq & mark
+        assert bool(((rank <= n_eq_kept[:, None]) == kept_tie)[eq].all()), f"{label}: tie rule violated"
+
+
+@pytest.mark.parametrize("name", ["C0", "C1", "C2", "C3", "C4"])
+def test_config_parity(torch_cuda, name):
+    torch = torch_cuda
+    cfg = synth.CONFIGS[name]
+    _say(f"{name}: generate {cfg}")
+    inputs = synth.generate(cfg)
+    _say(f"{name}: run GPU path")
+    dev, outs = run_gpu(torch, cfg, inputs)
+    scores = outs["scores"]
+    idx = outs["idx"]
+    rows = list(range(cfg.n_q)) if name == "C0" else sample_rows(cfg.n_q, cfg.seed)
+    _say(f"{name}: oracle on {len(rows)} rows")
+    ref = oracle.full_path(cfg, inputs, rows=rows)
+    g_scores = scores[rows].cpu().numpy()
+    assert np.array_equal(g_scores.view(np.uint32), ref["scores"].view(np.uint32)), f"{name}: scores differ"
+    g_idx = idx[rows].cpu().numpy()
+    assert np.array_equal(g_idx, ref["idx"]), f"{name}: indices differ"
+    check_attention(outs["out"][rows].cpu().numpy(), outs["lse"][rows].cpu().numpy(), ref["out"],
+                    ref["lse"], name)
+    _say(f"{name}: top-k properties on all rows")
+    check_topk_properties(torch, scores, idx, cfg.offset, cfg.top_k, name)
+    if name in ("C1", "C2"):
+        # whole score matrix against the oracle (bit-exact); cheap enough at 2k queries
+        all_ref = oracle.indexer_scores(cfg.n_q, cfg.offset, inputs["qidx"], inputs["w"], inputs["kidx"])
+        assert np.array_equal(scores.cpu().numpy().view(np.uint32), all_ref.view(np.uint32))
+
+
+def test_ragged_fast_path_all_rows(torch_cuda):
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C2"].replace(name="ragged", n_q=77, offset=1003, top_k=100, seed=31)
+    inputs = synth.generate(cfg)
+    ld = cfg.t_ctx + 3  # odd row stride: the select's unaligned path, -inf padding columns
+    _say(f"ragged: {cfg} ld={ld}")
+    dev, outs = run_gpu(torch, cfg, inputs, ld=ld)
+    ref = oracle.full_path(cfg, inputs)
+    ref_s = oracle.indexer_scores(cfg.n_q, cfg.offset, inputs["qidx"], inputs["w"], inputs["kidx"], ld=ld)
+    assert np.array_equal(outs["scores"].cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(outs["idx"].cpu().numpy(), ref["idx"])
+    check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], "ragged")
+
+
+def test_small_contexts_dense_and_hilo(torch_cuda):
+    # offset 0, 100 queries, k = 2048: every row is dense causal with 1..100
+    # keys, the few-key regime where P is split into hi + lo bf16 parts.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C1"].replace(name="dense_small", n_q=100, offset=0, seed=32)
+    inputs = synth.generate(cfg)
+    _say(f"dense_small: {cfg}")
+    dev, outs = run_gpu(torch, cfg, inputs)
+    ref = oracle.full_path(cfg, inputs)
+    assert np.array_equal(outs["idx"].cpu().numpy(), ref["idx"])
+    check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], "dense_small")
+    # single key: query 0 attends to key 0 only -> its value row, exactly
+    v0 = synth.bf16_bits_to_f32(inputs["kv"][0, : cfg.d_latent])
+    assert np.array_equal(outs["out"][0].cpu().numpy(), np.tile(v0, (cfg.n_heads, 1)))
+
+
+def test_topk_all_equal_scores_fallback(torch_cuda):
+    # q_idx = 0 -> every causal score is +0.0, so the k lowest indices win and
+    # the candidate set (the whole row) is larger than the select's LDS buffer.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C2"].replace(name="all_equal", n_q=40, offset=9000, seed=33)
+    inputs = synth.generate(cfg)
+    inputs["qidx"] = np.zeros_like(inputs["qidx"])
+    _say("all_equal")
+    dev, outs = run_gpu(torch, cfg, inputs)
+    s = outs["scores"].cpu().numpy()
+    for i in range(cfg.n_q):
+        assert np.all(s[i, : cfg.offset + i + 1].view(np.uint32) == 0)
+    exp = np.tile(np.arange(cfg.top_k, dtype=np.int32), (cfg.n_q, 1))
+    assert np.array_equal(outs["idx"].cpu().numpy(), exp)
+
+
+def test_topk_strictly_increasing_rows(torch_cuda):
+    # Distinct scores increasing with the key index: the last k causal keys win.
+    torch = torch_cuda
+    n_q, off, k = 33, 5000, 2048
+    ld = off + n_q
+    scores = torch.arange(ld, dtype=torch.float32, device="cuda").repeat(n_q, 1).contiguous()
+    idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off)
+    binding.topk_select(binding.make_dims(cfg), scores, ld, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for i in range(n_q):
+        p = off + i
+        assert np.array_equal(got[i], np.arange(p - k + 1, p + 1, dtype=np.int32))
+
+
+def test_topk_random_floats_and_negative_zero(torch_cuda):
+    # General fp32 scores (negatives, -0.0, +0.0, wide exponents) vs Python's sort.
+    torch = torch_cuda
+    rng = np.random.default_rng(77)
+    n_q, off, k = 24, 3000, 700
+    ld = off + n_q
+    s = (rng.standard_normal((n_q, ld)) * np.exp(rng.uniform(-20, 20, size=(n_q, ld)))).astype(np.float32)
+    s[rng.random(s.shape) < 0.05] = 0.0
+    s[rng.random(s.shape) < 0.05] = -0.0
+    s[:, 100:130] = 7.0  # a block of ties
+    for i in range(n_q):
+        s[i, off + i + 1:] = -np.inf
+    st = torch.from_numpy(s).cuda()
+    idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
+    binding.topk_select(binding.make_dims(cfg), st, ld, idx)
+    torch.cuda.synchronize()
+    ref = oracle.topk_select(n_q, off, k, s)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_attention_arbitrary_slots(torch_cuda):
+    # -1 padding anywhere, out-of-causal-range indices, a query with no valid
+    # slot (out = 0, lse = -inf), unsorted and repeated keys.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C2"].replace(name="slots", n_q=6, offset=3000, top_k=96, seed=34)
+    inputs = synth.generate(cfg)
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, cfg.offset, size=(cfg.n_q, cfg.top_k)).astype(np.int32)
+    idx[0, :] = -1
+    idx[1, rng.random(cfg.top_k) < 0.5] = -1
+    idx[2, :] = -1
+    idx[2, 50] = 17
+    idx[3, 10:20] = cfg.offset + 3 + 1  # one past query 3's position: skipped
+    idx[4, :] = 5  # the same key 96 times
+    dev = binding.to_device(inputs)
+    out = torch.empty((cfg.n_q, cfg.n_heads, cfg.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.n_q, cfg.n_heads), dtype=torch.float32, device="cuda")
+    gidx = torch.from_numpy(idx).cuda()
+    binding.sparse_mla_fwd(binding.make_dims(cfg), dev["q"], dev["kv"], gidx, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, inputs["q"],
+                                     inputs["kv"], idx)
+    assert np.all(out[0].cpu().numpy() == 0.0) and np.all(np.isneginf(lse[0].cpu().numpy()))
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "slots")
+
+
+def test_chunk_invariance_and_determinism(torch_cuda):
+    # The 8k chunk of C3 as four 2k chunks (offsets 8192, 10240, 12288, 14336)
+    # gives the same scores and index sets; repeating a call is bitwise stable.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C3"]
+    inputs = synth.generate(cfg)
+    _say("chunk invariance: whole chunk")
+    dev, outs = run_gpu(torch, cfg, inputs)
+    whole_idx = outs["idx"].clone()
+    whole_out = outs["out"].clone()
+    binding.run_chunk(cfg, dev, outs)
+    torch.cuda.synchronize()
+    assert torch.equal(outs["idx"], whole_idx) and torch.equal(outs["out"], whole_out)
+    for c in range(4):
+        sub = cfg.replace(n_q=2048, offset=cfg.offset + 2048 * c)
+        rows = slice(2048 * c, 2048 * (c + 1))
+        sdev = {"qidx": dev["qidx"][rows].contiguous(), "w": dev["w"][rows].contiguous(),
+                "q": dev["q"][rows].contiguous(), "kidx": dev["kidx"][: sub.t_ctx].contiguous(),
+                "kv": dev["kv"][: sub.t_ctx].contiguous()}
+        souts = binding.alloc_outputs(sub)
+        _say(f"chunk invariance: sub-chunk {c}")
+        binding.run_chunk(sub, sdev, souts)
+        torch.cuda.synchronize()
+        assert torch.equal(souts["idx"], whole_idx[rows])
+        assert torch.equal(souts["scores"], outs["scores"][rows, : sub.t_ctx])
