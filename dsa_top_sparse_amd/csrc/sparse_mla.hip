@@ -129,86 +129,116 @@ constexpr int kDR = 64;             // rope dims
 constexpr int kDQK = kDL + kDR;     // 576
 constexpr int kTile = 32;           // selected slots per tile
 constexpr int kThreads = 256;       // 4 waves
-constexpr int kKRowBytes = kDQK * 2;            // 1152: key-major row (72 x 16-byte pieces)
-constexpr int kKBufBytes = kTile * kKRowBytes;  // 36 KB
-constexpr int kVtBufBytes = kDL * kTile * 2;    // 32 KB: 512 dim-rows x 32 keys
-constexpr int kPBufBytes = kH * kTile * 2;      // 4 KB
+constexpr int kStages = 3;          // tiles resident in LDS (1 in use + 2 in flight)
+constexpr int kRowBytes = kDQK * 2;              // 1152 = 72 pieces of 16 bytes
+constexpr int kStageBytes = kTile * kRowBytes;   // 36 KB
+constexpr int kDmaPerWave = kStageBytes / (1024 * (kThreads / 64));  // 9 x 1 KB per wave per tile
+constexpr int kMaxTopk = 4096;      // the whole index row lives in LDS
 constexpr int kHiloMaxValid = 512;  // queries with at most this many valid keys use hi/lo P
+constexpr float kLazyLog2 = 8.0f;   // a head's reference max is raised only past +8 (log2)
 
-struct MlaSmem {
-  uint8_t kbuf[kKBufBytes];        // key-major tile, 16-byte pieces XOR-swizzled by row
-  uint8_t vtbuf[2][kVtBufBytes];   // dim-major tile (double-buffered)
-  uint8_t pbuf[2][kPBufBytes];     // P as bf16 [head][slot]: hi part, lo part
-  float alpha[kH];                 // per-head rescale of the running output
-  float fin[kH];                   // per-head 1 / l at the end
-  union {
-    uint32_t vbits;                // validity bit per slot of the staged tile
-    uint8_t vbyte[4];              // byte g: slots 8g..8g+7 (written by wave g)
-  };
-  int last_slot;                   // one past the last valid slot
-  int n_valid;
-};
 
-// Key-major piece s (0..71) of tile row r lives at piece s ^ (r & 7): a wave
-// reading one 16-byte piece of 16 rows, or 64 pieces of one row, touches every
-// LDS bank equally.
-__device__ __forceinline__ int kpiece_off(int r, int s) { return r * kKRowBytes + 16 * (s ^ (r & 7)); }
-
-// Dim d of the value tile lives in row (d % 8) * 64 + d / 8; its 32 keys form
-// 4 pieces of 8 keys, piece g stored at g ^ ((row >> 1) & 3). Both the
-// transposing writes (64 lanes -> 64 consecutive rows) and the MFMA operand
-// reads (16 dims x 4 pieces) then spread evenly over the banks.
-__device__ __forceinline__ int vrow(int d) { return (d & 7) * 64 + (d >> 3); }
-__device__ __forceinline__ int vpiece_off(int row, int g) { return row * 64 + 16 * (g ^ ((row >> 1) & 3)); }
+// Max / sum over the four lanes l16 + 16*q (q = 0..3) that hold one head, with
+// the gfx950 VALU lane swaps (xor-32, then xor-16 within each half).
+__device__ __forceinline__ float max_over_q4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_q4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __device__ __forceinline__ bool slot_valid(int32_t j, int64_t p) { return j >= 0 && (int64_t)j <= p; }
 
-// Registers one tile ahead: 8 value pieces (keys 8g..8g+7, dims 8c..8c+7) and
-// one rope piece (key rk, dims 512 + 8 rc .. +7).
-struct Gathered {
-  u32x4 v[8];
-  u32x4 r;
-  uint32_t vmask;  // bit e = key 8g + e valid
-  bool rvalid;
+struct MlaSmem {
+  uint8_t stage[kStages][kStageBytes];  // key-major tiles, 16-byte pieces swizzled per row
+  int32_t sidx[kMaxTopk];               // the query's slots: key, or -1 if not a valid key
+  uint32_t tmask[kMaxTopk / kTile];     // validity bit per slot, one word per tile
+  uint16_t pbuf[2][kH][kTile];          // P (bf16): hi part, lo part
+  float alpha[kH];                      // per-head rescale of the running output
+  int32_t rescale[4];                   // wave w raised a reference max of heads 16w.. this tile
+  float fin[kH];                        // per-head 1 / l at the end
+  int last_slot;                        // one past the last valid slot
+  int n_valid;
 };
 
-__device__ __forceinline__ void gather_issue(Gathered& G, const uint16_t* __restrict__ kv,
-                                             const int32_t* __restrict__ idx_row, int top_k, int tile,
-                                             int64_t p, int g, int c, int rk, int rc) {
-  G.vmask = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int slot = tile * kTile + 8 * g + e;
-    const int32_t j = slot < top_k ? idx_row[slot] : -1;
-    const bool ok = slot_valid(j, p);
-    G.vmask |= (uint32_t)ok << e;
-    G.v[e] = ok ? *reinterpret_cast<const u32x4*>(kv + (int64_t)j * kDQK + 8 * c) : u32x4{0, 0, 0, 0};
-  }
-  const int rslot = tile * kTile + rk;
-  const int32_t rj = rslot < top_k ? idx_row[rslot] : -1;
-  G.rvalid = slot_valid(rj, p);
-  G.r = G.rvalid ? *reinterpret_cast<const u32x4*>(kv + (int64_t)rj * kDQK + kDL + 8 * rc) : u32x4{0, 0, 0, 0};
+// Piece s (0..71, 8 dims each) of tile row r is stored at piece s ^ swz(r).
+// This swizzle spreads both operand reads evenly over the LDS banks: the Q K^T
+// reads (one piece of 16 rows) and the transposed P V reads (two pieces of 16
+// rows spaced 8G + e apart).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ (((r >> 3) & 3) << 1); }
+__device__ __forceinline__ int piece_off(int r, int s) { return r * kRowBytes + 16 * (s ^ swz(r)); }
+
+// Waits until at most N vector-memory operations of this wave are in flight
+// (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ void gather_commit(const Gathered& G, MlaSmem& sm, int vt, int g, int c, int rk,
-                                              int rc, int lane) {
-  // key-major copy
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// then synchronises. Unlike __syncthreads() it does not drain the direct-to-LDS
+// loads still in flight for later tiles; the tile about to be read is waited
+// for explicitly with wait_vmcnt before this barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Eight transposed 64-bit LDS reads (ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane j receives element j % 4 of the 4-element rows addressed by
+// lanes 4e + j / 4 (e = 0..3). Written as one asm statement that also waits for
+// the reads, so no read is in flight when the statement ends; the outputs are
+// early-clobber so that no destination can overlap an address. (As a builtin,
+// the compiler would drain the direct-to-LDS loads of later tiles before it.)
+__device__ __forceinline__ void read_tr8(uint64_t (&d)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+// Issues the direct-to-LDS loads of one tile: every wave writes 9 contiguous
+// 1 KB blocks of the stage; lane L of block m fills 16-byte slot 64m + L, whose
+// (row, piece) was precomputed in desc[]. Slots whose key is not valid load the
+// query's own row instead (always present, finite) and are masked in the
+// softmax, so every tile costs exactly kDmaPerWave loads per wave and the
+// vmcnt bookkeeping stays exact.
+__device__ __forceinline__ void issue_tile(MlaSmem& sm, const uint16_t* __restrict__ kv, int tile, int stage,
+                                           const uint32_t* desc, int wave, int64_t p) {
+  uint8_t* base = sm.stage[stage] + 1024 * (kDmaPerWave * wave);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(sm.kbuf + kpiece_off(8 * g + e, c)) = G.v[e];
-  *reinterpret_cast<u32x4*>(sm.kbuf + kpiece_off(rk, 64 + rc)) = G.r;
-  // transposed copy: for dim 8c + x, the 8 keys 8g..8g+7
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    u32x4 t;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a = G.v[2 * w][x >> 1], b = G.v[2 * w + 1][x >> 1];
-      t[w] = (x & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-    }
-    const int row = vrow(8 * c + x);
-    *reinterpret_cast<u32x4*>(sm.vtbuf[vt] + vpiece_off(row, g)) = t;
+  for (int u = 0; u < kDmaPerWave; ++u) {
+    const int r = desc[u] >> 8, piece = desc[u] & 0xFF;
+    const int32_t j = sm.sidx[tile * kTile + r];
+    const int64_t row = j >= 0 ? (int64_t)j : p;
+    const uint16_t* src = kv + row * kDQK + 8 * piece;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + 1024 * u), 16, 0, 0);
   }
-  if (lane == 0) sm.vbyte[g] = (uint8_t)G.vmask;
 }
 
 __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offset, int top_k, float scale_log2,
@@ -216,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
                                                                const uint16_t* __restrict__ kv,
                                                                const int32_t* __restrict__ idx,
                                                                float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ MlaSmem sm;
+  __shared__ __attribute__((aligned(1024))) MlaSmem sm;
   const int i = blockIdx.x;
   const int64_t p = (int64_t)offset + i;
   const int tid = threadIdx.x;
@@ -224,8 +254,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
   const int32_t* __restrict__ idx_row = idx + (int64_t)i * top_k;
+  const int n_slots = (top_k + kTile - 1) / kTile * kTile;
 
-  // Valid-slot census: early stop after the last valid slot; hi/lo P for few keys.
+  // ---- stage the index row (invalid slots -> -1), per-tile validity masks.
   if (tid == 0) {
     sm.last_slot = 0;
     sm.n_valid = 0;
@@ -233,8 +264,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   __syncthreads();
   {
     int last = 0, cnt = 0;
-    for (int t = tid; t < top_k; t += kThreads) {
-      if (slot_valid(idx_row[t], p)) {
+    for (int t0 = 0; t0 < n_slots; t0 += kThreads) {
+      const int t = t0 + tid;
+      int32_t j = -1;
+      if (t < top_k) j = idx_row[t];
+      const bool ok = t < top_k && slot_valid(j, p);
+      if (t < n_slots) sm.sidx[t] = ok ? j : -1;
+      const uint64_t b = __ballot(ok);
+      if (lane == 0 && t < n_slots) sm.tmask[t / kTile] = static_cast<uint32_t>(b);
+      if (lane == 32 && t < n_slots) sm.tmask[t / kTile] = static_cast<uint32_t>(b >> 32);
+      if (ok) {
         last = t + 1;
         ++cnt;
       }
@@ -252,47 +291,58 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   {
     const uint16_t* qsrc = q + ((int64_t)i * kH + 16 * wave + l16) * kDQK + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < kDQK / 32; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 32 * ks));
+    for (int ks = 0; ks < kDQK / 32; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 32 * ks));
   }
-  __syncthreads();
+  // This lane's DMA slots: slot P = 64 (9 wave + u) + lane -> (row, logical piece).
+  uint32_t desc[kDmaPerWave];
+#pragma unroll
+  for (int u = 0; u < kDmaPerWave; ++u) {
+    const int P = 64 * (kDmaPerWave * wave + u) + lane;
+    const int r = P / 72, pp = P - 72 * r;
+    desc[u] = (uint32_t)(r << 8) | (uint32_t)(pp ^ swz(r));
+  }
+  __syncthreads();  // sidx, tmask, counts visible (also drains the loads above)
   const int n_tiles = (sm.last_slot + kTile - 1) / kTile;
   const bool hilo = sm.n_valid <= kHiloMaxValid;
-
-  // Gather roles.
-  const int g = wave, c = lane;            // value pieces: keys 8g..8g+7, dims 8c..8c+7
-  const int rk = tid >> 3, rc = tid & 7;   // rope piece: key rk, dims 512 + 8rc..
 
   f32x4 o[4][8];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
-  float m_run = -INFINITY, l_run = 0.0f;  // for head 16*wave + l16
+  float m_ref = -INFINITY, l_part = 0.0f;  // head 16*wave + l16: reference max, partial sum
 
-  Gathered G;
-  if (n_tiles > 0) {
-    gather_issue(G, kv, idx_row, top_k, 0, p, g, c, rk, rc);
-    gather_commit(G, sm, 0, g, c, rk, rc, lane);
-  }
-  __syncthreads();
+  if (n_tiles > 0) issue_tile(sm, kv, 0, 0, desc, wave, p);
+  if (n_tiles > 1) issue_tile(sm, kv, 1, 1, desc, wave, p);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int vt = t & 1;
-    if (t + 1 < n_tiles) gather_issue(G, kv, idx_row, top_k, t + 1, p, g, c, rk, rc);
+    const int st = t % kStages;
+    if (t + 1 < n_tiles) wait_vmcnt<kDmaPerWave>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // tile t resident for every wave; iteration t-1 finished everywhere
+    if (t + 2 < n_tiles) issue_tile(sm, kv, t + 2, (t + 2) % kStages, desc, wave, p);
+    const uint8_t* __restrict__ tileb = sm.stage[st];
 
-    // ---- S^T = K Q^T for this wave's 16 heads: two 16-slot blocks.
-    f32x4 s[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+    // ---- S^T = K Q^T for this wave's 16 heads: two 16-slot blocks, each
+    // accumulated in two independent chains (even / odd k-steps).
+    f32x4 sacc[2][2] = {{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}, {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}};
 #pragma unroll
     for (int ks = 0; ks < kDQK / 32; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sm.kbuf + kpiece_off(16 * mb + l16, 4 * ks + q4)));
-        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[mb], 0, 0, 0);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tileb + piece_off(16 * mb + l16, 4 * ks + q4)));
+        sacc[mb][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[mb][ks & 1], 0, 0, 0);
       }
     }
-    // ---- online softmax for head 16*wave + l16 over slots 16mb + 4q4 + r.
-    const uint32_t vb = sm.vbits;
-    float tmax = -INFINITY;
+    f32x4 s[2] = {sacc[0][0] + sacc[0][1], sacc[1][0] + sacc[1][1]};
+    // ---- softmax for head 16*wave + l16 over slots 16mb + 4q4 + r, in the
+    // log2 domain. m_ref is the head's reference maximum: P = exp2(s - m_ref).
+    // It is only raised when a logit exceeds it by more than kLazyLog2, so P
+    // stays below 2^kLazyLog2 and the output rows need no rescaling on most
+    // tiles (the rows of a head are rescaled only on the tiles that raise it).
+    const uint32_t vb = sm.tmask[t];
+    float lmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -300,15 +350,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
         const int slot = 16 * mb + 4 * q4 + r;
         const float v = ((vb >> slot) & 1u) ? s[mb][r] * scale_log2 : -INFINITY;
         s[mb][r] = v;
-        tmax = fmaxf(tmax, v);
+        lmax = fmaxf(lmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = (m_run == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.0f;
+    bool rescaled = false;
+    float alpha = 1.0f;
+    if (__ballot(lmax > m_ref + kLazyLog2) != 0) {  // wave-uniform: some head must raise its reference
+      const float tmax = max_over_q4(lmax);
+      if (tmax > m_ref + kLazyLog2) {
+        alpha = (m_ref == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - tmax);  // O, l are 0 before the first key
+        m_ref = tmax;
+      }
+      rescaled = __ballot(alpha != 1.0f) != 0;
+      if (rescaled && q4 == 0) sm.alpha[16 * wave + l16] = alpha;
+    }
+    if (lane == 0) sm.rescale[wave] = rescaled ? 1 : 0;
     uint32_t phi[2][2], plo[2][2];
+    float psum = 0.0f;
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;  // a tile with no valid slot yet: P = 0
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float pv[4];
@@ -330,66 +388,72 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
         plo[mb][1] = pack_bf16x2(lo[2], lo[3]);
       }
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_part = l_part * alpha + psum;  // this lane's share of the head's sum
     {
       const int head = 16 * wave + l16;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int off = head * (kTile * 2) + 2 * (16 * mb + 4 * q4);
-        *reinterpret_cast<u32x2*>(sm.pbuf[0] + off) = u32x2{phi[mb][0], phi[mb][1]};
-        if (hilo) *reinterpret_cast<u32x2*>(sm.pbuf[1] + off) = u32x2{plo[mb][0], plo[mb][1]};
+        const int slot = 16 * mb + 4 * q4;
+        *reinterpret_cast<u32x2*>(&sm.pbuf[0][head][slot]) = u32x2{phi[mb][0], phi[mb][1]};
+        if (hilo) *reinterpret_cast<u32x2*>(&sm.pbuf[1][head][slot]) = u32x2{plo[mb][0], plo[mb][1]};
       }
-      if (q4 == 0) sm.alpha[head] = alpha;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- O[64 heads][dims 128w..] = alpha * O + P V.
+    // ---- O[64 heads][dims 128w..] = alpha * O + P V. The V operand comes
+    // straight from the key-major tile through transposed LDS reads: lane
+    // 16G + s (s = 4e + c) points at row 8G + 4h + e, dims 4c..4c+3 of the
+    // 16-dim block, and receives dims l16 of rows 8G + 4h + 0..3.
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const f32x4 al = *reinterpret_cast<const f32x4*>(&sm.alpha[16 * mb + 4 * q4]);
+      if (sm.rescale[mb]) {  // heads 16mb.. belong to wave mb; rare after the first tile
+        const f32x4 al = *reinterpret_cast<const f32x4*>(&sm.alpha[16 * mb + 4 * q4]);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[mb][nb] *= al;
+        for (int nb = 0; nb < 8; ++nb) o[mb][nb] *= al;
+      }
     }
-    {
-      bf16x8 pa[4];
+    bf16x8 pa[4], pl[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sm.pbuf[0] + (16 * mb + l16) * (kTile * 2) + 16 * q4));
+    for (int mb = 0; mb < 4; ++mb) {
+      pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.pbuf[0][16 * mb + l16][8 * q4]));
+      if (hilo) pl[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.pbuf[1][16 * mb + l16][8 * q4]));
+    }
+    const uint32_t tile_lds = lds_addr(tileb);
+    const int s16 = lane & 15;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int row = vrow(128 * wave + 16 * nb + l16);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sm.vtbuf[vt] + vpiece_off(row, q4)));
+    for (int blk = 0; blk < 2; ++blk) {
+      uint32_t a[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int nb = 4 * blk + (x >> 1), h = x & 1;
+        const int row = 8 * q4 + 4 * h + (s16 >> 2);
+        const int col = 128 * wave + 16 * nb + 4 * (s16 & 3);  // first of 4 dims
+        a[x] = tile_lds + row * kRowBytes + 16 * ((col >> 3) ^ swz(row)) + 2 * (col & 7);
+      }
+      uint64_t d[8];
+      read_tr8(d, a);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int nb = 4 * blk + x;
+        const u32x4 w = {(uint32_t)d[2 * x], (uint32_t)(d[2 * x] >> 32), (uint32_t)d[2 * x + 1],
+                         (uint32_t)(d[2 * x + 1] >> 32)};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], vf, o[mb][nb], 0, 0, 0);
-      }
-      if (hilo) {
+        if (hilo) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sm.pbuf[1] + (16 * mb + l16) * (kTile * 2) + 16 * q4));
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const int row = vrow(128 * wave + 16 * nb + l16);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sm.vtbuf[vt] + vpiece_off(row, q4)));
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], vf, o[mb][nb], 0, 0, 0);
+          for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[mb], vf, o[mb][nb], 0, 0, 0);
         }
       }
     }
-    // ---- stage the next tile (its loads were issued before Q K^T).
-    // kbuf and vbits were last read before the barrier above; the other value
-    // buffer was last read in the previous tile's P V.
-    if (t + 1 < n_tiles) gather_commit(G, sm, vt ^ 1, g, c, rk, rc, lane);
-    __syncthreads();
   }
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2.
+  const float l_run = sum_over_q4(l_part);
   if (q4 == 0) {
     const int head = 16 * wave + l16;
     sm.fin[head] = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
-    if (lse) lse[(int64_t)i * kH + head] = (l_run > 0.0f) ? (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f : -INFINITY;
+    if (lse) lse[(int64_t)i * kH + head] = (l_run > 0.0f) ? (m_ref + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f : -INFINITY;
   }
   __syncthreads();
   float* __restrict__ orow = out + (int64_t)i * kH * kDL;
@@ -406,7 +470,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 
 }  // namespace
 
-bool mla_fast_path(const MlaArgs& a) { return a.bf16 && a.n_heads == kH && a.d_latent == kDL && a.d_rope == kDR; }
+bool mla_fast_path(const MlaArgs& a) {
+  return a.bf16 && a.n_heads == kH && a.d_latent == kDL && a.d_rope == kDR && a.top_k <= kMaxTopk;
+}
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
