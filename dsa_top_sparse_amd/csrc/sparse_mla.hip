@@ -128,15 +128,13 @@ constexpr int kDL = 512;            // latent / value dims
 constexpr int kDR = 64;             // rope dims
 constexpr int kDQK = kDL + kDR;     // 576
 constexpr int kTile = 32;           // selected slots per tile
-constexpr int kThreads = 256;       // 4 waves
+constexpr int kThreads = 512;       // 8 waves (two per SIMD)
 constexpr int kStages = 3;          // tiles resident in LDS (1 in use + 2 in flight)
 constexpr int kRowBytes = kDQK * 2;              // 1152 = 72 pieces of 16 bytes
 constexpr int kStageBytes = kTile * kRowBytes;   // 36 KB
-constexpr int kDmaPerWave = kStageBytes / (1024 * (kThreads / 64));  // 9 x 1 KB per wave per tile
 constexpr int kMaxTopk = 4096;      // the whole index row lives in LDS
 constexpr int kHiloMaxValid = 512;  // queries with at most this many valid keys use hi/lo P
-constexpr float kLazyLog2 = 8.0f;   // a head's reference max is raised only past +8 (log2)
-
+constexpr float kRefLog2 = 64.0f;   // P = exp2(s - m_ref) < 2^64 before a restart is forced
 
 // Max / sum over the four lanes l16 + 16*q (q = 0..3) that hold one head, with
 // the gfx950 VALU lane swaps (xor-32, then xor-16 within each half).
@@ -155,24 +153,36 @@ __device__ __forceinline__ float sum_over_q4(float x) {
 
 __device__ __forceinline__ bool slot_valid(int32_t j, int64_t p) { return j >= 0 && (int64_t)j <= p; }
 
+// Two fp32 -> packed bf16 pair (round to nearest even, hardware conversion).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
 struct MlaSmem {
-  uint8_t stage[kStages][kStageBytes];  // key-major tiles, 16-byte pieces swizzled per row
+  uint8_t stage[kStages][kStageBytes];  // tiles: [32 rows][1 KB latent] then [32 rows][128 B rope]
   int32_t sidx[kMaxTopk];               // the query's slots: key, or -1 if not a valid key
   uint32_t tmask[kMaxTopk / kTile];     // validity bit per slot, one word per tile
   uint16_t pbuf[2][kH][kTile];          // P (bf16): hi part, lo part
-  float alpha[kH];                      // per-head rescale of the running output
-  int32_t rescale[4];                   // wave w raised a reference max of heads 16w.. this tile
-  float fin[kH];                        // per-head 1 / l at the end
+  f32x4 sx[4][2][64];                   // Q K^T partial sums exchanged between the two k-halves
+  float hmax[2][kH];                    // per key half: a head's max over the tile (reference exchange)
+  float hsum[2][kH];                    // per key half: a head's row sum (epilogue)
+  int32_t restart;                      // a head raised its reference: restart the query
   int last_slot;                        // one past the last valid slot
+  int first_tile;                       // first tile holding a valid slot
   int n_valid;
 };
 
-// Piece s (0..71, 8 dims each) of tile row r is stored at piece s ^ swz(r).
-// This swizzle spreads both operand reads evenly over the LDS banks: the Q K^T
-// reads (one piece of 16 rows) and the transposed P V reads (two pieces of 16
-// rows spaced 8G + e apart).
+// A stage holds the 32 rows of a tile as a 1 KB latent part per row (pieces
+// 0..63, 8 dims each) followed by a 128-byte rope part per row (pieces
+// 64..71). Piece s of row r is stored at position s ^ swz(r) within its part
+// (the XOR touches only the low 3 bits). The swizzle spreads both operand
+// reads evenly over the LDS banks: the Q K^T reads (one piece of 16 rows) and
+// the transposed P V reads (two pieces of 16 rows spaced 8G + e apart).
+constexpr int kLatBytes = 1024;
+constexpr int kRopeOff = kTile * kLatBytes;  // 32 KB
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ (((r >> 3) & 3) << 1); }
-__device__ __forceinline__ int piece_off(int r, int s) { return r * kRowBytes + 16 * (s ^ swz(r)); }
 
 // Waits until at most N vector-memory operations of this wave are in flight
 // (expcnt and lgkmcnt left unconstrained).
@@ -222,25 +232,90 @@ __device__ __forceinline__ void read_tr8(uint64_t (&d)[8], const uint32_t (&a)[8
       : "memory");
 }
 
-// Issues the direct-to-LDS loads of one tile: every wave writes 9 contiguous
-// 1 KB blocks of the stage; lane L of block m fills 16-byte slot 64m + L, whose
-// (row, piece) was precomputed in desc[]. Slots whose key is not valid load the
-// query's own row instead (always present, finite) and are masked in the
-// softmax, so every tile costs exactly kDmaPerWave loads per wave and the
-// vmcnt bookkeeping stays exact.
-__device__ __forceinline__ void issue_tile(MlaSmem& sm, const uint16_t* __restrict__ kv, int tile, int stage,
-                                           const uint32_t* desc, int wave, int64_t p) {
-  uint8_t* base = sm.stage[stage] + 1024 * (kDmaPerWave * wave);
+// Direct-to-LDS loads of one tile: 36 blocks of 1 KB. Block m < 32 is the
+// latent part of row m (lane L loads piece L ^ swz(m)); block 32 + b holds the
+// rope parts of rows 8b .. 8b+7 (lane L: row 8b + L/8, piece (L % 8) ^ swz(row)).
+// Waves 0-3 issue blocks 5w .. 5w+4, waves 4-7 blocks 20 + 4(w-4) .. +3.
+// Slots whose key is not valid load the query's own row instead (always
+// present, finite) and are masked in the softmax, so every tile costs a fixed
+// number of loads per wave and the vmcnt bookkeeping stays exact. Addresses
+// are 32-bit byte offsets from the cache base (the host checks that the cache
+// is below 4 GiB).
+__device__ __forceinline__ void dma_block(MlaSmem& sm, const uint8_t* __restrict__ kv, int tile, int stage, int m,
+                                          int lane, uint32_t p) {
+  const int32_t* sidx = sm.sidx + tile * kTile;
+  uint8_t* dst = sm.stage[stage] + kLatBytes * m;
+  uint32_t off;
+  if (m < kTile) {
+    const int32_t j = __builtin_amdgcn_readfirstlane(sidx[m]);
+    const uint32_t row = j >= 0 ? (uint32_t)j : p;
+    off = row * (uint32_t)kRowBytes + 16u * (uint32_t)(lane ^ swz(m));
+  } else {
+    const int r = 8 * (m - kTile) + (lane >> 3);
+    const int32_t j = sidx[r];
+    const uint32_t row = j >= 0 ? (uint32_t)j : p;
+    off = row * (uint32_t)kRowBytes + 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swz(r));
+  }
+  // 16 bytes per lane to LDS address M0 + 16 * lane. Issued from asm: with the
+  // builtin, the compiler cannot tell which LDS reads alias the DMA and drains
+  // every load in flight before the next tile's operand reads. There is no
+  // register output to track; M0 is set here and used by nothing else in this
+  // kernel; completion is tracked with the explicit vmcnt waits above.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(kv), "s"(lds_addr(dst))
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+__device__ __forceinline__ void issue_tile(MlaSmem& sm, const uint8_t* __restrict__ kv, int tile, int stage, int wave,
+                                           int lane, uint32_t p) {
+  if (wave < 4) {
 #pragma unroll
-  for (int u = 0; u < kDmaPerWave; ++u) {
-    const int r = desc[u] >> 8, piece = desc[u] & 0xFF;
-    const int32_t j = sm.sidx[tile * kTile + r];
-    const int64_t row = j >= 0 ? (int64_t)j : p;
-    const uint16_t* src = kv + row * kDQK + 8 * piece;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + 1024 * u), 16, 0, 0);
+    for (int u = 0; u < 5; ++u) dma_block(sm, kv, tile, stage, 5 * wave + u, lane, p);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dma_block(sm, kv, tile, stage, 20 + 4 * (wave - 4) + u, lane, p);
+  }
+}
+// Waits until this wave's loads of the tile about to be read have landed,
+// leaving the next tile's loads (if any) in flight.
+__device__ __forceinline__ void wait_tile(int wave, bool next_in_flight) {
+  if (!next_in_flight) wait_vmcnt<0>();
+  else if (wave < 4) wait_vmcnt<5>();
+  else wait_vmcnt<4>();
+}
+
+template <bool HILO>
+__device__ __forceinline__ void pv_tile(f32x4 (&o)[4][4], const MlaSmem& sm, uint32_t tile_lds,
+                                        const uint32_t (&tr_base)[8], int l16, int q4) {
+  uint32_t a[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) a[x] = tile_lds + tr_base[x];  // x = 2 nb + h
+  uint64_t d[8];
+  read_tr8(d, a);
+  bf16x8 vf[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    vf[nb] = __builtin_bit_cast(bf16x8, (u32x4{(uint32_t)d[2 * nb], (uint32_t)(d[2 * nb] >> 32), (uint32_t)d[2 * nb + 1],
+                                               (uint32_t)(d[2 * nb + 1] >> 32)}));
+#pragma unroll
+  for (int part = 0; part < (HILO ? 2 : 1); ++part) {
+    bf16x8 pa[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.pbuf[part][16 * mb + l16][8 * q4]));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], vf[nb], o[mb][nb], 0, 0, 0);
   }
 }
 
+// One workgroup (8 waves, two per SIMD) per query.
+//   Q K^T : wave w = 4 kd + hg covers heads 16 hg .. +15, all 32 slots of the
+//           tile, and the k-steps of parity kd (32 dims each); the two halves
+//           are summed through LDS, after which wave w owns slots 16 kd .. +15;
+//   P V   : wave w covers output dims 64 w .. +63 for all 64 heads.
 __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offset, int top_k, float scale_log2,
                                                                const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ kv,
@@ -252,18 +327,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 3, kd = wave >> 2;  // head group; k-step parity, later key half
   const int l16 = lane & 15, q4 = lane >> 4;
+  const int head = 16 * hg + l16;            // this lane's head in Q K^T / softmax
   const int32_t* __restrict__ idx_row = idx + (int64_t)i * top_k;
   const int n_slots = (top_k + kTile - 1) / kTile * kTile;
+  const uint8_t* __restrict__ kvb = reinterpret_cast<const uint8_t*>(kv);
 
   // ---- stage the index row (invalid slots -> -1), per-tile validity masks.
   if (tid == 0) {
     sm.last_slot = 0;
     sm.n_valid = 0;
+    sm.restart = 0;
+    sm.first_tile = 0x7fffffff;
   }
   __syncthreads();
   {
-    int last = 0, cnt = 0;
+    int last = 0, cnt = 0, first = 0x7fffffff;
     for (int t0 = 0; t0 < n_slots; t0 += kThreads) {
       const int t = t0 + tid;
       int32_t j = -1;
@@ -275,196 +355,188 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
       if (lane == 32 && t < n_slots) sm.tmask[t / kTile] = static_cast<uint32_t>(b >> 32);
       if (ok) {
         last = t + 1;
+        first = min(first, t / kTile);
         ++cnt;
       }
     }
     last = (int)wave_max((float)last);  // exact: slots < 2^24
     cnt = wave_sum_int(cnt);
+    first = -(int)wave_max(-(float)first);
     if (lane == 0) {
       atomicMax(&sm.last_slot, last);
       atomicAdd(&sm.n_valid, cnt);
+      atomicMin(&sm.first_tile, first);
     }
   }
 
-  // Q fragments (B operand of S^T = K Q^T): head 16*wave + l16, dims 32ks + 8q4 .. +7.
-  bf16x8 qf[kDQK / 32];
+  // Q fragments (B operand of S^T = K Q^T): head 16 hg + l16, k-step 2u + kd,
+  // dims 32 (2u + kd) + 8 q4 .. +7.
+  bf16x8 qf[9];
   {
-    const uint16_t* qsrc = q + ((int64_t)i * kH + 16 * wave + l16) * kDQK + 8 * q4;
+    const uint16_t* qsrc = q + ((int64_t)i * kH + head) * kDQK + 32 * kd + 8 * q4;
 #pragma unroll
-    for (int ks = 0; ks < kDQK / 32; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 32 * ks));
+    for (int u = 0; u < 9; ++u) qf[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 64 * u));
   }
-  // This lane's DMA slots: slot P = 64 (9 wave + u) + lane -> (row, logical piece).
-  uint32_t desc[kDmaPerWave];
+  // Stage offsets of this lane's Q K^T operand pieces: row 16 mb + l16, piece
+  // 8u + 4kd + q4 (latent part for u < 8, rope part for u = 8).
+  uint32_t qk_lat[2], qk_rope[2];
 #pragma unroll
-  for (int u = 0; u < kDmaPerWave; ++u) {
-    const int P = 64 * (kDmaPerWave * wave + u) + lane;
-    const int r = P / 72, pp = P - 72 * r;
-    desc[u] = (uint32_t)(r << 8) | (uint32_t)(pp ^ swz(r));
+  for (int mb = 0; mb < 2; ++mb) {
+    const int row = 16 * mb + l16;
+    const int pc = (4 * kd + q4) ^ swz(row);
+    qk_lat[mb] = row * kLatBytes + 16 * pc;
+    qk_rope[mb] = kRopeOff + row * 128 + 16 * pc;
   }
-  __syncthreads();  // sidx, tmask, counts visible (also drains the loads above)
+  // Transposed P V operand reads: lane 16G + s (s = 4e + c) addresses row
+  // 8G + 4h + e, dims 64w + 16nb + 4c .. +3 (piece 8w + 2nb + c/2, byte
+  // 8 (c % 2) inside it); entry x = 2 nb + h.
+  uint32_t tr_base[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int nb = x >> 1, h = x & 1, e = l16 >> 2, c = l16 & 3;
+    const int row = 8 * q4 + 4 * h + e;
+    tr_base[x] = row * kLatBytes + 128 * wave + 16 * ((2 * nb + (c >> 1)) ^ swz(row)) + 8 * (c & 1);
+  }
+  __syncthreads();  // sidx, tmask, counts visible
+  // Every load above (the Q fragments in particular) completes here, on every
+  // path into the tile loop: inside the loop the only vector-memory operations
+  // are the tile loads, whose count the explicit vmcnt waits rely on.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
   const int n_tiles = (sm.last_slot + kTile - 1) / kTile;
+  const int first_tile = sm.first_tile;
   const bool hilo = sm.n_valid <= kHiloMaxValid;
+  const uint32_t p32 = (uint32_t)p;
 
-  f32x4 o[4][8];
+  f32x4 o[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
-  float m_ref = -INFINITY, l_part = 0.0f;  // head 16*wave + l16: reference max, partial sum
+    for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
+  float m_ref = -INFINITY, l_part = 0.0f;  // this lane's head: reference (log2), partial sum
 
-  if (n_tiles > 0) issue_tile(sm, kv, 0, 0, desc, wave, p);
-  if (n_tiles > 1) issue_tile(sm, kv, 1, 1, desc, wave, p);
+  if (n_tiles > 0) issue_tile(sm, kvb, 0, 0, wave, lane, p32);
+  if (n_tiles > 1) issue_tile(sm, kvb, 1, 1, wave, lane, p32);
+  // Each restart happens at a later tile than the previous one, so n_tiles
+  // restarts always suffice; the cap only guarantees termination.
+  int restarts_left = n_tiles;
 
   for (int t = 0; t < n_tiles; ++t) {
     const int st = t % kStages;
-    if (t + 1 < n_tiles) wait_vmcnt<kDmaPerWave>();
-    else wait_vmcnt<0>();
+    wait_tile(wave, t + 1 < n_tiles);
     lds_barrier();  // tile t resident for every wave; iteration t-1 finished everywhere
-    if (t + 2 < n_tiles) issue_tile(sm, kv, t + 2, (t + 2) % kStages, desc, wave, p);
+    if (t + 2 < n_tiles) issue_tile(sm, kvb, t + 2, (t + 2) % kStages, wave, lane, p32);
     const uint8_t* __restrict__ tileb = sm.stage[st];
 
-    // ---- S^T = K Q^T for this wave's 16 heads: two 16-slot blocks, each
-    // accumulated in two independent chains (even / odd k-steps).
-    f32x4 sacc[2][2] = {{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}, {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}};
+    // ---- partial S^T = K Q^T over this wave's k-steps, both 16-slot blocks.
+    f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
 #pragma unroll
-    for (int ks = 0; ks < kDQK / 32; ++ks) {
+    for (int u = 0; u < 9; ++u) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tileb + piece_off(16 * mb + l16, 4 * ks + q4)));
-        sacc[mb][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[mb][ks & 1], 0, 0, 0);
+        const uint8_t* src = (u < 8) ? tileb + qk_lat[mb] + 128 * u : tileb + qk_rope[mb];
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src));
+        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[u], sacc[mb], 0, 0, 0);
       }
+      if (u == 4) __builtin_amdgcn_sched_barrier(0);  // bounds how far operand reads are hoisted
     }
-    f32x4 s[2] = {sacc[0][0] + sacc[0][1], sacc[1][0] + sacc[1][1]};
-    // ---- softmax for head 16*wave + l16 over slots 16mb + 4q4 + r, in the
-    // log2 domain. m_ref is the head's reference maximum: P = exp2(s - m_ref).
-    // It is only raised when a logit exceeds it by more than kLazyLog2, so P
-    // stays below 2^kLazyLog2 and the output rows need no rescaling on most
-    // tiles (the rows of a head are rescaled only on the tiles that raise it).
+    // Hand the other slot block's partial to the partner wave, keep block kd.
+    sm.sx[hg][1 - kd][lane] = sacc[1 - kd];
+    lds_barrier();
+    const f32x4 other = sm.sx[hg][kd][lane];
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (sacc[kd][r] + other[r]) * scale_log2;
+
+    // ---- softmax for this lane's head over slots 16 kd + 4 q4 + r, in the
+    // log2 domain, P = exp2(s - m_ref). m_ref is agreed by the two key-half
+    // waves of the head at the first tile with a valid slot and may lag the
+    // true maximum by up to kRefLog2, so P < 2^kRefLog2 (exact in relative
+    // terms in bf16 and fp32) and the output accumulators are never rescaled
+    // inside the loop. A logit beyond m_ref + kRefLog2 raises the reference and
+    // restarts the query from its first tile with zeroed accumulators; each
+    // restart happens at a later tile than the previous one.
     const uint32_t vb = sm.tmask[t];
-    float lmax = -INFINITY;
+    if (vb != 0xFFFFFFFFu) {  // partially valid tile (block-uniform)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int slot = 16 * mb + 4 * q4 + r;
-        const float v = ((vb >> slot) & 1u) ? s[mb][r] * scale_log2 : -INFINITY;
-        s[mb][r] = v;
-        lmax = fmaxf(lmax, v);
-      }
-    bool rescaled = false;
-    float alpha = 1.0f;
-    if (__ballot(lmax > m_ref + kLazyLog2) != 0) {  // wave-uniform: some head must raise its reference
-      const float tmax = max_over_q4(lmax);
-      if (tmax > m_ref + kLazyLog2) {
-        alpha = (m_ref == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - tmax);  // O, l are 0 before the first key
-        m_ref = tmax;
-      }
-      rescaled = __ballot(alpha != 1.0f) != 0;
-      if (rescaled && q4 == 0) sm.alpha[16 * wave + l16] = alpha;
+      for (int r = 0; r < 4; ++r) sv[r] = ((vb >> (16 * kd + 4 * q4 + r)) & 1u) ? sv[r] : -INFINITY;
     }
-    if (lane == 0) sm.rescale[wave] = rescaled ? 1 : 0;
-    uint32_t phi[2][2], plo[2][2];
-    float psum = 0.0f;
-    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;  // a tile with no valid slot yet: P = 0
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      float pv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(s[mb][r] - m_use);
-        psum += pv[r];
-      }
-      phi[mb][0] = pack_bf16x2(pv[0], pv[1]);
-      phi[mb][1] = pack_bf16x2(pv[2], pv[3]);
-      if (hilo) {
-        float lo[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t hb = (r < 2 ? phi[mb][0] : phi[mb][1]) >> (16 * (r & 1));
-          lo[r] = pv[r] - bf16_to_f32((uint16_t)(hb & 0xFFFFu));
-        }
-        plo[mb][0] = pack_bf16x2(lo[0], lo[1]);
-        plo[mb][1] = pack_bf16x2(lo[2], lo[3]);
-      }
+    const float lmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    if (t == first_tile) {  // block-uniform: agree on the references (one extra barrier per query)
+      const float hm = max_over_q4(lmax);
+      if (q4 == 0) sm.hmax[kd][head] = hm;
+      lds_barrier();
+      // Never lowers the reference: after a restart this tile is replayed and
+      // the raised value must survive, or the restart would repeat.
+      m_ref = fmaxf(m_ref, fmaxf(sm.hmax[0][head], sm.hmax[1][head]));
+    } else if (__ballot(lmax > m_ref + kRefLog2) != 0) {
+      if (max_over_q4(lmax) > m_ref + kRefLog2) sm.restart = 1;
     }
-    l_part = l_part * alpha + psum;  // this lane's share of the head's sum
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;  // before the first valid tile: P = 0
+    float pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(sv[r] - m_use);
+    l_part += (pv[0] + pv[1]) + (pv[2] + pv[3]);
     {
-      const int head = 16 * wave + l16;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int slot = 16 * mb + 4 * q4;
-        *reinterpret_cast<u32x2*>(&sm.pbuf[0][head][slot]) = u32x2{phi[mb][0], phi[mb][1]};
-        if (hilo) *reinterpret_cast<u32x2*>(&sm.pbuf[1][head][slot]) = u32x2{plo[mb][0], plo[mb][1]};
+      const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
+      const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
+      *reinterpret_cast<u32x2*>(&sm.pbuf[0][head][16 * kd + 4 * q4]) = u32x2{h0, h1};
+      if (hilo) {
+        const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
+        const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
+        *reinterpret_cast<u32x2*>(&sm.pbuf[1][head][16 * kd + 4 * q4]) = u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)};
       }
     }
     lds_barrier();
 
-    // ---- O[64 heads][dims 128w..] = alpha * O + P V. The V operand comes
-    // straight from the key-major tile through transposed LDS reads: lane
-    // 16G + s (s = 4e + c) points at row 8G + 4h + e, dims 4c..4c+3 of the
-    // 16-dim block, and receives dims l16 of rows 8G + 4h + 0..3.
+    if (sm.restart && restarts_left > 0) {  // block-uniform (written before the barrier above); rare
+      --restarts_left;
+      const float hm = max_over_q4(lmax);
+      if (q4 == 0) sm.hmax[kd][head] = hm;
+      wait_vmcnt<0>();  // drain the loads of later tiles
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (sm.rescale[mb]) {  // heads 16mb.. belong to wave mb; rare after the first tile
-        const f32x4 al = *reinterpret_cast<const f32x4*>(&sm.alpha[16 * mb + 4 * q4]);
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) o[mb][nb] *= al;
-      }
+        for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
+      l_part = 0.0f;
+      lds_barrier();  // flag read everywhere, maxima published; nobody reads a stage or P now
+      m_ref = fmaxf(m_ref, fmaxf(sm.hmax[0][head], sm.hmax[1][head]));
+      if (tid == 0) sm.restart = 0;
+      issue_tile(sm, kvb, 0, 0, wave, lane, p32);
+      if (n_tiles > 1) issue_tile(sm, kvb, 1, 1, wave, lane, p32);
+      t = -1;
+      continue;
     }
-    bf16x8 pa[4], pl[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.pbuf[0][16 * mb + l16][8 * q4]));
-      if (hilo) pl[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.pbuf[1][16 * mb + l16][8 * q4]));
-    }
+    // ---- O[64 heads][dims 64w..] += P V, V read straight from the tile's
+    // latent part through transposed LDS reads.
     const uint32_t tile_lds = lds_addr(tileb);
-    const int s16 = lane & 15;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      uint32_t a[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int nb = 4 * blk + (x >> 1), h = x & 1;
-        const int row = 8 * q4 + 4 * h + (s16 >> 2);
-        const int col = 128 * wave + 16 * nb + 4 * (s16 & 3);  // first of 4 dims
-        a[x] = tile_lds + row * kRowBytes + 16 * ((col >> 3) ^ swz(row)) + 2 * (col & 7);
-      }
-      uint64_t d[8];
-      read_tr8(d, a);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int nb = 4 * blk + x;
-        const u32x4 w = {(uint32_t)d[2 * x], (uint32_t)(d[2 * x] >> 32), (uint32_t)d[2 * x + 1],
-                         (uint32_t)(d[2 * x + 1] >> 32)};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], vf, o[mb][nb], 0, 0, 0);
-        if (hilo) {
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[mb], vf, o[mb][nb], 0, 0, 0);
-        }
-      }
-    }
+    if (hilo) pv_tile<true>(o, sm, tile_lds, tr_base, l16, q4);
+    else pv_tile<false>(o, sm, tile_lds, tr_base, l16, q4);
   }
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2.
-  const float l_run = sum_over_q4(l_part);
-  if (q4 == 0) {
-    const int head = 16 * wave + l16;
-    sm.fin[head] = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+  const float lh = sum_over_q4(l_part);
+  if (q4 == 0) sm.hsum[kd][head] = lh;
+  __syncthreads();
+  if (wave < 4 && q4 == 0) {
+    const float l_run = sm.hsum[0][head] + sm.hsum[1][head];
     if (lse) lse[(int64_t)i * kH + head] = (l_run > 0.0f) ? (m_ref + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f : -INFINITY;
   }
-  __syncthreads();
   float* __restrict__ orow = out + (int64_t)i * kH * kDL;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const f32x4 f = *reinterpret_cast<const f32x4*>(&sm.fin[16 * mb + 4 * q4]);
+    float f[4];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 16 * mb + 4 * q4 + r;
+      const float l_run = sm.hsum[0][hh] + sm.hsum[1][hh];
+      f[r] = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        orow[(int64_t)(16 * mb + 4 * q4 + r) * kDL + 128 * wave + 16 * nb + l16] = o[mb][nb][r] * f[r];
+        orow[(int64_t)(16 * mb + 4 * q4 + r) * kDL + 64 * wave + 16 * nb + l16] = o[mb][nb][r] * f[r];
   }
 }
 

@@ -269,3 +269,27 @@ def test_chunk_invariance_and_determinism(torch_cuda):
         torch.cuda.synchronize()
         assert torch.equal(souts["idx"], whole_idx[rows])
         assert torch.equal(souts["scores"], outs["scores"][rows, : sub.t_ctx])
+
+
+def test_attention_reference_restart(torch_cuda):
+    # One selected key, in a late tile, is aligned with head 5's query so that
+    # its logit exceeds every logit of the first tile by ~60 (natural log):
+    # far beyond the lag the kernel lets its per-head reference maximum keep,
+    # so the query must restart with a raised reference.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C2"].replace(name="restart", n_q=4, offset=3000, seed=35)
+    inputs = synth.generate(cfg)
+    rng = np.random.default_rng(9)
+    idx = np.sort(rng.choice(cfg.offset, size=(cfg.n_q, cfg.top_k), replace=True), axis=1).astype(np.int32)
+    j = int(idx[0, 700])  # tile 21 of query 0
+    q5 = synth.bf16_bits_to_f32(inputs["q"][0, 5]).astype(np.float64)
+    kvj = 60.0 * q5 / (np.linalg.norm(q5) ** 2) / cfg.sm_scale  # q5 . kvj * scale = 60
+    inputs["kv"][j] = synth.f32_to_bf16_bits(kvj.astype(np.float32))
+    dev = binding.to_device(inputs)
+    out = torch.empty((cfg.n_q, cfg.n_heads, cfg.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.n_q, cfg.n_heads), dtype=torch.float32, device="cuda")
+    binding.sparse_mla_fwd(binding.make_dims(cfg), dev["q"], dev["kv"], torch.from_numpy(idx).cuda(), out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, inputs["q"], inputs["kv"], idx)
+    assert ref_l[0, 5] > 55.0  # the planted logit dominates head 5
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "restart")
