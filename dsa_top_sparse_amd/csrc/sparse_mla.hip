@@ -164,7 +164,7 @@ struct MlaSmem {
   uint8_t stage[kStages][kStageBytes];  // tiles: [32 rows][1 KB latent] then [32 rows][128 B rope]
   int32_t sidx[kMaxTopk];               // the query's slots: key, or -1 if not a valid key
   uint32_t tmask[kMaxTopk / kTile];     // validity bit per slot, one word per tile
-  uint16_t pbuf[2][kH][kTile];          // P (bf16): hi part, lo part
+  uint8_t pbuf[2][kH * kTile * 2];      // P (bf16, chunk-swizzled rows): hi part, lo part
   f32x4 sx[4][2][64];                   // Q K^T partial sums exchanged between the two k-halves
   float hmax[2][kH];                    // per key half: a head's max over the tile (reference exchange)
   float hsum[2][kH];                    // per key half: a head's row sum (epilogue)
@@ -176,13 +176,21 @@ struct MlaSmem {
 
 // A stage holds the 32 rows of a tile as a 1 KB latent part per row (pieces
 // 0..63, 8 dims each) followed by a 128-byte rope part per row (pieces
-// 64..71). Piece s of row r is stored at position s ^ swz(r) within its part
-// (the XOR touches only the low 3 bits). The swizzle spreads both operand
-// reads evenly over the LDS banks: the Q K^T reads (one piece of 16 rows) and
-// the transposed P V reads (two pieces of 16 rows spaced 8G + e apart).
+// 64..71). The LDS has 64 banks of 4 bytes, i.e. 16 positions of 16 bytes per
+// bank cycle. Latent piece s of row r is stored at s ^ (r & 15) (the XOR stays
+// within aligned groups of 16 pieces); rope piece s of row r at s ^ ((r >> 1) & 7).
+// Both operand reads then spread over all banks: a Q K^T read (one piece of 16
+// consecutive rows) and a transposed P V read (two pieces of 16 rows 8G + e).
 constexpr int kLatBytes = 1024;
 constexpr int kRopeOff = kTile * kLatBytes;  // 32 KB
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ (((r >> 3) & 3) << 1); }
+__device__ __forceinline__ int swl(int r) { return r & 15; }
+__device__ __forceinline__ int swr(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int lat_off(int r, int s) { return r * kLatBytes + 16 * (s ^ swl(r)); }
+__device__ __forceinline__ int rope_off(int r, int s) { return kRopeOff + r * 128 + 16 * (s ^ swr(r)); }
+// P rows (one per head, 32 bf16 = 64 bytes = 4 chunks of 8 slots): chunk c of
+// head h is stored at c ^ ((h >> 2) & 3), which keeps both the 8-byte softmax
+// writes and the 16-byte operand reads free of bank conflicts.
+__device__ __forceinline__ int p_off(int h, int c) { return h * 64 + 16 * (c ^ ((h >> 2) & 3)); }
 
 // Waits until at most N vector-memory operations of this wave are in flight
 // (expcnt and lgkmcnt left unconstrained).
@@ -233,48 +241,43 @@ __device__ __forceinline__ void read_tr8(uint64_t (&d)[8], const uint32_t (&a)[8
 }
 
 // Direct-to-LDS loads of one tile: 36 blocks of 1 KB. Block m < 32 is the
-// latent part of row m (lane L loads piece L ^ swz(m)); block 32 + b holds the
-// rope parts of rows 8b .. 8b+7 (lane L: row 8b + L/8, piece (L % 8) ^ swz(row)).
-// Waves 0-3 issue blocks 5w .. 5w+4, waves 4-7 blocks 20 + 4(w-4) .. +3.
+// latent part of row m (lane L fills position L, i.e. loads piece L ^ (m & 15));
+// block 32 + b holds the rope parts of rows 8b .. 8b+7 (lane L fills position
+// L % 8 of row 8b + L/8, i.e. loads rope piece (L % 8) ^ swr(row)).
+// Wave w issues the latent blocks 4w .. 4w+3, and waves 0-3 also rope block w.
 // Slots whose key is not valid load the query's own row instead (always
 // present, finite) and are masked in the softmax, so every tile costs a fixed
 // number of loads per wave and the vmcnt bookkeeping stays exact. Addresses
 // are 32-bit byte offsets from the cache base (the host checks that the cache
-// is below 4 GiB).
-__device__ __forceinline__ void dma_block(MlaSmem& sm, const uint8_t* __restrict__ kv, int tile, int stage, int m,
-                                          int lane, uint32_t p) {
-  const int32_t* sidx = sm.sidx + tile * kTile;
-  uint8_t* dst = sm.stage[stage] + kLatBytes * m;
-  uint32_t off;
-  if (m < kTile) {
-    const int32_t j = __builtin_amdgcn_readfirstlane(sidx[m]);
-    const uint32_t row = j >= 0 ? (uint32_t)j : p;
-    off = row * (uint32_t)kRowBytes + 16u * (uint32_t)(lane ^ swz(m));
-  } else {
-    const int r = 8 * (m - kTile) + (lane >> 3);
-    const int32_t j = sidx[r];
-    const uint32_t row = j >= 0 ? (uint32_t)j : p;
-    off = row * (uint32_t)kRowBytes + 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swz(r));
-  }
-  // 16 bytes per lane to LDS address M0 + 16 * lane. Issued from asm: with the
-  // builtin, the compiler cannot tell which LDS reads alias the DMA and drains
-  // every load in flight before the next tile's operand reads. There is no
-  // register output to track; M0 is set here and used by nothing else in this
-  // kernel; completion is tracked with the explicit vmcnt waits above.
+// is below 4 GiB). Each load is issued from asm: with the builtin, the compiler
+// cannot tell which LDS reads alias the DMA and drains every load in flight
+// before the next tile's operand reads. There is no register output to track;
+// M0 is set here and used by nothing else in this kernel; completion is
+// tracked with the explicit vmcnt waits of the tile loop.
+__device__ __forceinline__ void dma16(const uint8_t* __restrict__ kv, uint32_t off, uint32_t lds) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(kv), "s"(lds_addr(dst))
-               : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(kv), "s"(lds) : "memory", "m0");
 #pragma clang diagnostic pop
 }
 __device__ __forceinline__ void issue_tile(MlaSmem& sm, const uint8_t* __restrict__ kv, int tile, int stage, int wave,
                                            int lane, uint32_t p) {
+  const int32_t* sidx = sm.sidx + tile * kTile;
+  const int32_t jl = sidx[lane & 31];                    // lane l: slot l % 32 (latent rows)
+  const int rr = 8 * (wave & 3) + (lane >> 3);           // rope row of this lane
+  const int32_t jr = sidx[rr];
+  const uint32_t stage_lds = lds_addr(sm.stage[stage]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int m = 4 * wave + u;
+    const int32_t j = __builtin_amdgcn_readlane(jl, m);  // wave-uniform
+    const uint32_t row = j >= 0 ? (uint32_t)j : p;
+    dma16(kv, row * (uint32_t)kRowBytes + 16u * (uint32_t)(lane ^ swl(m)), stage_lds + kLatBytes * m);
+  }
   if (wave < 4) {
-#pragma unroll
-    for (int u = 0; u < 5; ++u) dma_block(sm, kv, tile, stage, 5 * wave + u, lane, p);
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dma_block(sm, kv, tile, stage, 20 + 4 * (wave - 4) + u, lane, p);
+    const uint32_t row = jr >= 0 ? (uint32_t)jr : p;
+    dma16(kv, row * (uint32_t)kRowBytes + 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swr(rr)),
+          stage_lds + kRopeOff + 1024 * wave);
   }
 }
 // Waits until this wave's loads of the tile about to be read have landed,
@@ -303,7 +306,7 @@ __device__ __forceinline__ void pv_tile(f32x4 (&o)[4][4], const MlaSmem& sm, uin
     bf16x8 pa[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.pbuf[part][16 * mb + l16][8 * q4]));
+      pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sm.pbuf[part] + p_off(16 * mb + l16, q4)));
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -377,15 +380,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 #pragma unroll
     for (int u = 0; u < 9; ++u) qf[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 64 * u));
   }
-  // Stage offsets of this lane's Q K^T operand pieces: row 16 mb + l16, piece
-  // 8u + 4kd + q4 (latent part for u < 8, rope part for u = 8).
-  uint32_t qk_lat[2], qk_rope[2];
+  // Stage offsets of this lane's Q K^T operand pieces: piece 8u + 4kd + q4
+  // (latent part for u < 8, rope part for u = 8) of row 16 kd + l16 (the slot
+  // block this wave keeps, x = 0) and of row 16 (1 - kd) + l16 (the block it
+  // hands over, x = 1). For u < 8 the swizzle depends on u only through u % 2,
+  // so the address is qk_lat[x][u % 2] + 256 (u / 2).
+  uint32_t qk_lat[2][2], qk_rope[2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int row = 16 * mb + l16;
-    const int pc = (4 * kd + q4) ^ swz(row);
-    qk_lat[mb] = row * kLatBytes + 16 * pc;
-    qk_rope[mb] = kRopeOff + row * 128 + 16 * pc;
+  for (int x = 0; x < 2; ++x) {
+    const int row = 16 * (x == 0 ? kd : 1 - kd) + l16;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) qk_lat[x][par] = lat_off(row, 8 * par + 4 * kd + q4);
+    qk_rope[x] = rope_off(row, 4 * kd + q4);
   }
   // Transposed P V operand reads: lane 16G + s (s = 4e + c) addresses row
   // 8G + 4h + e, dims 64w + 16nb + 4c .. +3 (piece 8w + 2nb + c/2, byte
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   for (int x = 0; x < 8; ++x) {
     const int nb = x >> 1, h = x & 1, e = l16 >> 2, c = l16 & 3;
     const int row = 8 * q4 + 4 * h + e;
-    tr_base[x] = row * kLatBytes + 128 * wave + 16 * ((2 * nb + (c >> 1)) ^ swz(row)) + 8 * (c & 1);
+    tr_base[x] = lat_off(row, 8 * wave + 2 * nb + (c >> 1)) + 8 * (c & 1);
   }
   __syncthreads();  // sidx, tmask, counts visible
   // Every load above (the Q fragments in particular) completes here, on every
@@ -421,32 +427,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   // restarts always suffice; the cap only guarantees termination.
   int restarts_left = n_tiles;
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int st = t % kStages;
+  int st = 0;  // stage of tile t; tile t + 2 goes to stage (st + 2) % 3
+  for (int t = 0; t < n_tiles; ++t, st = (st == kStages - 1) ? 0 : st + 1) {
     wait_tile(wave, t + 1 < n_tiles);
     lds_barrier();  // tile t resident for every wave; iteration t-1 finished everywhere
-    if (t + 2 < n_tiles) issue_tile(sm, kvb, t + 2, (t + 2) % kStages, wave, lane, p32);
+    if (t + 2 < n_tiles) issue_tile(sm, kvb, t + 2, st == 0 ? 2 : st - 1, wave, lane, p32);
     const uint8_t* __restrict__ tileb = sm.stage[st];
 
     // ---- partial S^T = K Q^T over this wave's k-steps, both 16-slot blocks.
-    f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+    f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};  // [0] own block, [1] other block
 #pragma unroll
     for (int u = 0; u < 9; ++u) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const uint8_t* src = (u < 8) ? tileb + qk_lat[mb] + 128 * u : tileb + qk_rope[mb];
+      for (int x = 0; x < 2; ++x) {
+        const uint8_t* src = (u < 8) ? tileb + qk_lat[x][u & 1] + 256 * (u >> 1) : tileb + qk_rope[x];
         const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src));
-        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[u], sacc[mb], 0, 0, 0);
+        sacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[u], sacc[x], 0, 0, 0);
       }
       if (u == 4) __builtin_amdgcn_sched_barrier(0);  // bounds how far operand reads are hoisted
     }
-    // Hand the other slot block's partial to the partner wave, keep block kd.
-    sm.sx[hg][1 - kd][lane] = sacc[1 - kd];
+    // Hand the other block's partial to the partner wave, add the partner's
+    // partial of the own block.
+    sm.sx[hg][1 - kd][lane] = sacc[1];
     lds_barrier();
     const f32x4 other = sm.sx[hg][kd][lane];
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (sacc[kd][r] + other[r]) * scale_log2;
+    for (int r = 0; r < 4; ++r) sv[r] = (sacc[0][r] + other[r]) * scale_log2;
 
     // ---- softmax for this lane's head over slots 16 kd + 4 q4 + r, in the
     // log2 domain, P = exp2(s - m_ref). m_ref is agreed by the two key-half
@@ -480,11 +487,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     {
       const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
       const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
-      *reinterpret_cast<u32x2*>(&sm.pbuf[0][head][16 * kd + 4 * q4]) = u32x2{h0, h1};
+      const int poff = p_off(head, 2 * kd + (q4 >> 1)) + 8 * (q4 & 1);  // slots 16 kd + 4 q4 .. +3
+      *reinterpret_cast<u32x2*>(sm.pbuf[0] + poff) = u32x2{h0, h1};
       if (hilo) {
         const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
         const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
-        *reinterpret_cast<u32x2*>(&sm.pbuf[1][head][16 * kd + 4 * q4]) = u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)};
+        *reinterpret_cast<u32x2*>(sm.pbuf[1] + poff) = u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)};
       }
     }
     lds_barrier();
@@ -505,6 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
       issue_tile(sm, kvb, 0, 0, wave, lane, p32);
       if (n_tiles > 1) issue_tile(sm, kvb, 1, 1, wave, lane, p32);
       t = -1;
+      st = kStages - 1;  // the loop increment brings it to stage 0 with t = 0
       continue;
     }
     // ---- O[64 heads][dims 64w..] += P V, V read straight from the tile's
