@@ -28,6 +28,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 namespace {
@@ -128,13 +130,14 @@ constexpr int kDL = 512;            // latent / value dims
 constexpr int kDR = 64;             // rope dims
 constexpr int kDQK = kDL + kDR;     // 576
 constexpr int kTile = 32;           // selected slots per tile
-constexpr int kThreads = 512;       // 8 waves (two per SIMD)
-constexpr int kStages = 3;          // tiles resident in LDS (1 in use + 2 in flight)
+constexpr int kThreads = 512;       // 8 waves: 4 score waves + 4 gather / P V waves
+constexpr int kStages = 4;          // LDS tile stages (hi/lo queries use 3; P's lo part takes the 4th)
 constexpr int kRowBytes = kDQK * 2;              // 1152 = 72 pieces of 16 bytes
 constexpr int kStageBytes = kTile * kRowBytes;   // 36 KB
-constexpr int kMaxTopk = 4096;      // the whole index row lives in LDS
+constexpr int kRingTiles = 24;      // index ring: 3 parts of 8 tiles (1 KB each)
 constexpr int kHiloMaxValid = 512;  // queries with at most this many valid keys use hi/lo P
 constexpr float kRefLog2 = 64.0f;   // P = exp2(s - m_ref) < 2^64 before a restart is forced
+constexpr int kGatherLoads = 9;     // loads per tile and gather wave: 8 latent rows + one rope block
 
 // Max / sum over the four lanes l16 + 16*q (q = 0..3) that hold one head, with
 // the gfx950 VALU lane swaps (xor-32, then xor-16 within each half).
@@ -162,16 +165,12 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 
 struct MlaSmem {
   uint8_t stage[kStages][kStageBytes];  // tiles: [32 rows][1 KB latent] then [32 rows][128 B rope]
-  int32_t sidx[kMaxTopk];               // the query's slots: key, or -1 if not a valid key
-  uint32_t tmask[kMaxTopk / kTile];     // validity bit per slot, one word per tile
-  uint8_t pbuf[2][kH * kTile * 2];      // P (bf16, chunk-swizzled rows): hi part, lo part
-  f32x4 sx[4][2][64];                   // Q K^T partial sums exchanged between the two k-halves
-  float hmax[2][kH];                    // per key half: a head's max over the tile (reference exchange)
-  float hsum[2][kH];                    // per key half: a head's row sum (epilogue)
-  int32_t restart;                      // a head raised its reference: restart the query
-  int last_slot;                        // one past the last valid slot
-  int first_tile;                       // first tile holding a valid slot
-  int n_valid;
+  uint8_t pbuf[2][kH * kTile * 2];      // P hi part (bf16, chunk-swizzled rows) by tile parity
+  int32_t ring[kRingTiles][kTile];      // the query's index row, tile t at t % 24
+  float hmax[2][2][kH];                 // [tile parity][slot half][head]: the head's max over that half
+  float lsum[2][kH];                    // [slot half][head]: softmax denominators at the end
+  int32_t restart[2];                   // [tile parity]: a head needs a higher reference, restart
+  int32_t c_last, c_valid, c_first;     // index row census
 };
 
 // A stage holds the 32 rows of a tile as a 1 KB latent part per row (pieces
@@ -202,8 +201,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
 // then synchronises. Unlike __syncthreads() it does not drain the direct-to-LDS
-// loads still in flight for later tiles; the tile about to be read is waited
-// for explicitly with wait_vmcnt before this barrier.
+// loads still in flight for later tiles; a tile about to be read is waited for
+// explicitly with wait_vmcnt before the barrier.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -211,348 +210,429 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // 32-bit LDS address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-
-// Eight transposed 64-bit LDS reads (ds_read_b64_tr_b16): within each group of
-// 16 lanes, lane j receives element j % 4 of the 4-element rows addressed by
-// lanes 4e + j / 4 (e = 0..3). Written as one asm statement that also waits for
-// the reads, so no read is in flight when the statement ends; the outputs are
-// early-clobber so that no destination can overlap an address. (As a builtin,
-// the compiler would drain the direct-to-LDS loads of later tiles before it.)
-__device__ __forceinline__ void read_tr8(uint64_t (&d)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+__device__ __forceinline__ u32x4 lds_read16(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((lds_u8*)(uintptr_t)a);
+}
+__device__ __forceinline__ s16x4 lds_read_tr(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u8*)(uintptr_t)a));
 }
 
-// Direct-to-LDS loads of one tile: 36 blocks of 1 KB. Block m < 32 is the
-// latent part of row m (lane L fills position L, i.e. loads piece L ^ (m & 15));
-// block 32 + b holds the rope parts of rows 8b .. 8b+7 (lane L fills position
-// L % 8 of row 8b + L/8, i.e. loads rope piece (L % 8) ^ swr(row)).
-// Wave w issues the latent blocks 4w .. 4w+3, and waves 0-3 also rope block w.
-// Slots whose key is not valid load the query's own row instead (always
-// present, finite) and are masked in the softmax, so every tile costs a fixed
-// number of loads per wave and the vmcnt bookkeeping stays exact. Addresses
-// are 32-bit byte offsets from the cache base (the host checks that the cache
-// is below 4 GiB). Each load is issued from asm: with the builtin, the compiler
-// cannot tell which LDS reads alias the DMA and drains every load in flight
-// before the next tile's operand reads. There is no register output to track;
-// M0 is set here and used by nothing else in this kernel; completion is
-// tracked with the explicit vmcnt waits of the tile loop.
-__device__ __forceinline__ void dma16(const uint8_t* __restrict__ kv, uint32_t off, uint32_t lds) {
+// One direct-to-LDS load: 16 bytes per lane from base + off to LDS address
+// lds + 16 * lane. Issued from asm: with the builtin, the compiler cannot tell
+// which LDS reads alias the load and drains every load in flight before the
+// next tile's operand reads. There is no register output to track; M0 is set
+// here and used by nothing else in this kernel; completion is tracked with the
+// explicit vmcnt waits of the tile loop.
+__device__ __forceinline__ void dma16(const void* __restrict__ base, uint32_t off, uint32_t lds) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(kv), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "m0");
 #pragma clang diagnostic pop
 }
-__device__ __forceinline__ void issue_tile(MlaSmem& sm, const uint8_t* __restrict__ kv, int tile, int stage, int wave,
-                                           int lane, uint32_t p) {
-  const int32_t* sidx = sm.sidx + tile * kTile;
-  const int32_t jl = sidx[lane & 31];                    // lane l: slot l % 32 (latent rows)
-  const int rr = 8 * (wave & 3) + (lane >> 3);           // rope row of this lane
-  const int32_t jr = sidx[rr];
-  const uint32_t stage_lds = lds_addr(sm.stage[stage]);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int m = 4 * wave + u;
-    const int32_t j = __builtin_amdgcn_readlane(jl, m);  // wave-uniform
-    const uint32_t row = j >= 0 ? (uint32_t)j : p;
-    dma16(kv, row * (uint32_t)kRowBytes + 16u * (uint32_t)(lane ^ swl(m)), stage_lds + kLatBytes * m);
-  }
-  if (wave < 4) {
-    const uint32_t row = jr >= 0 ? (uint32_t)jr : p;
-    dma16(kv, row * (uint32_t)kRowBytes + 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swr(rr)),
-          stage_lds + kRopeOff + 1024 * wave);
-  }
-}
-// Waits until this wave's loads of the tile about to be read have landed,
-// leaving the next tile's loads (if any) in flight.
-__device__ __forceinline__ void wait_tile(int wave, bool next_in_flight) {
-  if (!next_in_flight) wait_vmcnt<0>();
-  else if (wave < 4) wait_vmcnt<5>();
-  else wait_vmcnt<4>();
+
+// Byte offset of a selected row in the cache; slots past top_k or holding no
+// valid key load the query's own row instead (always present, finite) and are
+// masked in the softmax, so that every tile costs a fixed number of loads.
+// The offsets are 32-bit (the host checks that the cache is below 4 GiB).
+__device__ __forceinline__ uint32_t row_off(int32_t j, int slot, int top_k, uint32_t p) {
+  return ((slot < top_k && j >= 0 && (uint32_t)j <= p) ? (uint32_t)j : p) * (uint32_t)kRowBytes;
 }
 
-template <bool HILO>
-__device__ __forceinline__ void pv_tile(f32x4 (&o)[4][4], const MlaSmem& sm, uint32_t tile_lds,
-                                        const uint32_t (&tr_base)[8], int l16, int q4) {
-  uint32_t a[8];
+// Gather of one tile by gather wave v (slots 8v .. 8v+7): the latent parts of
+// its 8 rows (1 KB each; lane L fills position L of row m = 8v + u, i.e. loads
+// piece L ^ swl(m)) and their rope parts (one 1 KB load; lane L fills position
+// L % 8 of row 8v + L / 8, i.e. loads rope piece (L % 8) ^ swr(row)). `roff` is
+// lane L's row offset for slot 8v + L / 8.
+__device__ __forceinline__ void gather_tile(const uint8_t* __restrict__ kv, uint32_t roff, uint32_t stage_lds, int v,
+                                            uint32_t lane16, uint32_t rope_lane) {
 #pragma unroll
-  for (int x = 0; x < 8; ++x) a[x] = tile_lds + tr_base[x];  // x = 2 nb + h
-  uint64_t d[8];
-  read_tr8(d, a);
-  bf16x8 vf[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    vf[nb] = __builtin_bit_cast(bf16x8, (u32x4{(uint32_t)d[2 * nb], (uint32_t)(d[2 * nb] >> 32), (uint32_t)d[2 * nb + 1],
-                                               (uint32_t)(d[2 * nb + 1] >> 32)}));
-#pragma unroll
-  for (int part = 0; part < (HILO ? 2 : 1); ++part) {
-    bf16x8 pa[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      pa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sm.pbuf[part] + p_off(16 * mb + l16, q4)));
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], vf[nb], o[mb][nb], 0, 0, 0);
+  for (int u = 0; u < 8; ++u) {
+    const int m = 8 * v + u;
+    const uint32_t row = __builtin_amdgcn_readlane(roff, 8 * u);  // wave-uniform
+    dma16(kv + row, lane16 ^ (uint32_t)(16 * (m & 15)), stage_lds + kLatBytes * m);
   }
+  dma16(kv, roff + rope_lane, stage_lds + kRopeOff + 1024 * v);
 }
 
-// One workgroup (8 waves, two per SIMD) per query.
-//   Q K^T : wave w = 4 kd + hg covers heads 16 hg .. +15, all 32 slots of the
-//           tile, and the k-steps of parity kd (32 dims each); the two halves
-//           are summed through LDS, after which wave w owns slots 16 kd .. +15;
-//   P V   : wave w covers output dims 64 w .. +63 for all 64 heads.
+// Index ring refill: tiles 8c .. 8c+7 of the index row (1 KB) into ring part
+// c % 3. Lanes whose 16 bytes would pass the end of the row read the row's
+// last 16 bytes instead; their slots lie past top_k and are never used.
+__device__ __forceinline__ void issue_ring(MlaSmem& sm, const int32_t* __restrict__ idx_row, int c, int top_k,
+                                           int lane) {
+  int s0 = 256 * c + 4 * lane;
+  if (s0 + 4 > top_k) s0 = top_k - 4;
+  dma16(idx_row, 4u * (uint32_t)s0, lds_addr(sm.ring[8 * (c % 3)]));
+}
+
+// One workgroup (8 waves, two per SIMD) per query, in two roles that run side
+// by side on every SIMD and meet at one barrier per tile:
+//   score waves (w = 0..3; g = w & 1, s = w >> 1): S^T = K Q^T for heads
+//     32 g .. +31 and slots 16 s .. +15 of a tile over all 576 dims (the
+//     query's Q fragments for those heads stay in registers), then the
+//     softmax of those scores; P goes to LDS as bf16;
+//   gather / P V waves (w = 4..7; v = w - 4): the direct-to-LDS loads of
+//     slots 8v .. 8v+7 of the tiles two ahead, and O += P V for output dims
+//     128 v .. +127 of all 64 heads.
+// In iteration t the score waves work on tile t while the P V waves work on
+// tile t - 1; tiles t + 1 and t + 2 are in flight (4 stages).
+//
+// The softmax needs no running rescale: every head gets a fixed reference
+// m_ref (log2 domain), its maximum over the first tile with a valid slot, and
+// P = exp2(s - m_ref) stays below 2^kRefLog2 until a logit exceeds
+// m_ref + kRefLog2; then the query restarts from tile 0 with the reference
+// raised to that tile's maximum (a later tile each time, so it ends).
 __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offset, int top_k, float scale_log2,
                                                                const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ kv,
                                                                const int32_t* __restrict__ idx,
                                                                float* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) MlaSmem sm;
-  const int i = blockIdx.x;
+  const int i = n_q - 1 - (int)blockIdx.x;  // latest queries (most keys) first
   const int64_t p = (int64_t)offset + i;
+  const uint32_t p32 = (uint32_t)p;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wave & 3, kd = wave >> 2;  // head group; k-step parity, later key half
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int head = 16 * hg + l16;            // this lane's head in Q K^T / softmax
   const int32_t* __restrict__ idx_row = idx + (int64_t)i * top_k;
-  const int n_slots = (top_k + kTile - 1) / kTile * kTile;
-  const uint8_t* __restrict__ kvb = reinterpret_cast<const uint8_t*>(kv);
 
-  // ---- stage the index row (invalid slots -> -1), per-tile validity masks.
+  // ---- census of the index row: valid slots, last valid slot, first valid tile.
   if (tid == 0) {
-    sm.last_slot = 0;
-    sm.n_valid = 0;
-    sm.restart = 0;
-    sm.first_tile = 0x7fffffff;
+    sm.c_last = 0;
+    sm.c_valid = 0;
+    sm.c_first = 0x7fffffff;
+    sm.restart[0] = 0;
+    sm.restart[1] = 0;
   }
   __syncthreads();
   {
     int last = 0, cnt = 0, first = 0x7fffffff;
-    for (int t0 = 0; t0 < n_slots; t0 += kThreads) {
-      const int t = t0 + tid;
-      int32_t j = -1;
-      if (t < top_k) j = idx_row[t];
-      const bool ok = t < top_k && slot_valid(j, p);
-      if (t < n_slots) sm.sidx[t] = ok ? j : -1;
-      const uint64_t b = __ballot(ok);
-      if (lane == 0 && t < n_slots) sm.tmask[t / kTile] = static_cast<uint32_t>(b);
-      if (lane == 32 && t < n_slots) sm.tmask[t / kTile] = static_cast<uint32_t>(b >> 32);
-      if (ok) {
+    for (int t = tid; t < top_k; t += kThreads) {
+      if (slot_valid(idx_row[t], p)) {
         last = t + 1;
         first = min(first, t / kTile);
         ++cnt;
       }
     }
-    last = (int)wave_max((float)last);  // exact: slots < 2^24
+    last = wave_max_int(last);
     cnt = wave_sum_int(cnt);
-    first = -(int)wave_max(-(float)first);
+    first = wave_min_int(first);
     if (lane == 0) {
-      atomicMax(&sm.last_slot, last);
-      atomicAdd(&sm.n_valid, cnt);
-      atomicMin(&sm.first_tile, first);
+      atomicMax(&sm.c_last, last);
+      atomicAdd(&sm.c_valid, cnt);
+      atomicMin(&sm.c_first, first);
     }
   }
-
-  // Q fragments (B operand of S^T = K Q^T): head 16 hg + l16, k-step 2u + kd,
-  // dims 32 (2u + kd) + 8 q4 .. +7.
-  bf16x8 qf[9];
-  {
-    const uint16_t* qsrc = q + ((int64_t)i * kH + head) * kDQK + 32 * kd + 8 * q4;
-#pragma unroll
-    for (int u = 0; u < 9; ++u) qf[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 64 * u));
+  if (wave == 7) {  // index ring: tiles 0..15
+    issue_ring(sm, idx_row, 0, top_k, lane);
+    issue_ring(sm, idx_row, 1, top_k, lane);
   }
-  // Stage offsets of this lane's Q K^T operand pieces: piece 8u + 4kd + q4
-  // (latent part for u < 8, rope part for u = 8) of row 16 kd + l16 (the slot
-  // block this wave keeps, x = 0) and of row 16 (1 - kd) + l16 (the block it
-  // hands over, x = 1). For u < 8 the swizzle depends on u only through u % 2,
-  // so the address is qk_lat[x][u % 2] + 256 (u / 2).
-  uint32_t qk_lat[2][2], qk_rope[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int row = 16 * (x == 0 ? kd : 1 - kd) + l16;
-#pragma unroll
-    for (int par = 0; par < 2; ++par) qk_lat[x][par] = lat_off(row, 8 * par + 4 * kd + q4);
-    qk_rope[x] = rope_off(row, 4 * kd + q4);
-  }
-  // Transposed P V operand reads: lane 16G + s (s = 4e + c) addresses row
-  // 8G + 4h + e, dims 64w + 16nb + 4c .. +3 (piece 8w + 2nb + c/2, byte
-  // 8 (c % 2) inside it); entry x = 2 nb + h.
-  uint32_t tr_base[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int nb = x >> 1, h = x & 1, e = l16 >> 2, c = l16 & 3;
-    const int row = 8 * q4 + 4 * h + e;
-    tr_base[x] = lat_off(row, 8 * wave + 2 * nb + (c >> 1)) + 8 * (c & 1);
-  }
-  __syncthreads();  // sidx, tmask, counts visible
-  // Every load above (the Q fragments in particular) completes here, on every
-  // path into the tile loop: inside the loop the only vector-memory operations
-  // are the tile loads, whose count the explicit vmcnt waits rely on.
+  // Every load above completes here: inside the tile loop the only
+  // vector-memory operations are the tile and ring loads, whose counts the
+  // explicit vmcnt waits rely on.
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
-  const int n_tiles = (sm.last_slot + kTile - 1) / kTile;
-  const int first_tile = sm.first_tile;
-  const bool hilo = sm.n_valid <= kHiloMaxValid;
-  const uint32_t p32 = (uint32_t)p;
-
-  f32x4 o[4][4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
-  float m_ref = -INFINITY, l_part = 0.0f;  // this lane's head: reference (log2), partial sum
-
-  if (n_tiles > 0) issue_tile(sm, kvb, 0, 0, wave, lane, p32);
-  if (n_tiles > 1) issue_tile(sm, kvb, 1, 1, wave, lane, p32);
-  // Each restart happens at a later tile than the previous one, so n_tiles
-  // restarts always suffice; the cap only guarantees termination.
+  __syncthreads();  // census and ring visible
+  const int n_tiles = (sm.c_last + kTile - 1) / kTile;
+  const int first_tile = sm.c_first;
+  const bool hilo = sm.c_valid <= kHiloMaxValid;
+  const uint32_t stage0_lds = lds_addr(sm.stage[0]);
   int restarts_left = n_tiles;
 
-  int st = 0;  // stage of tile t; tile t + 2 goes to stage (st + 2) % 3
-  for (int t = 0; t < n_tiles; ++t, st = (st == kStages - 1) ? 0 : st + 1) {
-    wait_tile(wave, t + 1 < n_tiles);
-    lds_barrier();  // tile t resident for every wave; iteration t-1 finished everywhere
-    if (t + 2 < n_tiles) issue_tile(sm, kvb, t + 2, st == 0 ? 2 : st - 1, wave, lane, p32);
-    const uint8_t* __restrict__ tileb = sm.stage[st];
+  // ================================================================ score waves
+  auto score_role = [&](auto hilo_c) {
+    constexpr bool HILO = decltype(hilo_c)::value;
+    constexpr int S = HILO ? kStages - 1 : kStages;
+    const int g = wave & 1, s = wave >> 1;
+    int head[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) head[hb] = 32 * g + 16 * hb + l16;
+    // Q fragments (B operand): head[hb], k-step u covers dims 32u + 8 q4 .. +7.
+    bf16x8 qf[2][18];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const uint16_t* qsrc = q + ((int64_t)i * kH + head[hb]) * kDQK + 8 * q4;
+#pragma unroll
+      for (int u = 0; u < 18; ++u) qf[hb][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 32 * u));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    // K operand (A): row 16 s + l16 of the tile, piece 4u + q4. For u < 16 the
+    // swizzle keeps the piece inside its group of 16, so the offset is
+    // qk_lat[u % 4] + 256 (u / 4); the rope k-steps u = 16, 17 have their own.
+    const int krow = 16 * s + l16;
+    uint32_t qk_lat[4], qk_rope[2];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) qk_lat[x] = lat_off(krow, 4 * x + q4);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) qk_rope[x] = rope_off(krow, 4 * x + q4);
+    // P write position of this lane's 4 slots 16 s + 4 q4 .. +3 in each head row.
+    int poff[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) poff[hb] = p_off(head[hb], 2 * s + (q4 >> 1)) + 8 * (q4 & 1);
 
-    // ---- partial S^T = K Q^T over this wave's k-steps, both 16-slot blocks.
-    f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};  // [0] own block, [1] other block
+    auto qk = [&](f32x4 (&sacc)[2], uint32_t tile_lds) {
+      sacc[0] = f32x4{0, 0, 0, 0};
+      sacc[1] = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int u = 0; u < 9; ++u) {
+      for (int u = 0; u < 18; ++u) {
+        const uint32_t a = tile_lds + (u < 16 ? qk_lat[u & 3] + 256 * (u >> 2) : qk_rope[u - 16]);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_read16(a));
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const uint8_t* src = (u < 8) ? tileb + qk_lat[x][u & 1] + 256 * (u >> 1) : tileb + qk_rope[x];
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src));
-        sacc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[u], sacc[x], 0, 0, 0);
+        for (int hb = 0; hb < 2; ++hb) sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[hb][u], sacc[hb], 0, 0, 0);
       }
-      if (u == 4) __builtin_amdgcn_sched_barrier(0);  // bounds how far operand reads are hoisted
-    }
-    // Hand the other block's partial to the partner wave, add the partner's
-    // partial of the own block.
-    sm.sx[hg][1 - kd][lane] = sacc[1];
-    lds_barrier();
-    const f32x4 other = sm.sx[hg][kd][lane];
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (sacc[0][r] + other[r]) * scale_log2;
+    };
 
-    // ---- softmax for this lane's head over slots 16 kd + 4 q4 + r, in the
-    // log2 domain, P = exp2(s - m_ref). m_ref is agreed by the two key-half
-    // waves of the head at the first tile with a valid slot and may lag the
-    // true maximum by up to kRefLog2, so P < 2^kRefLog2 (exact in relative
-    // terms in bf16 and fp32) and the output accumulators are never rescaled
-    // inside the loop. A logit beyond m_ref + kRefLog2 raises the reference and
-    // restarts the query from its first tile with zeroed accumulators; each
-    // restart happens at a later tile than the previous one.
-    const uint32_t vb = sm.tmask[t];
-    if (vb != 0xFFFFFFFFu) {  // partially valid tile (block-uniform)
+    float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.0f, 0.0f};
+    if (n_tiles > 0) {  // reference prologue on the first tile with a valid slot
+      uint32_t vmask = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = ((vb >> (16 * kd + 4 * q4 + r)) & 1u) ? sv[r] : -INFINITY;
-    }
-    const float lmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    if (t == first_tile) {  // block-uniform: agree on the references (one extra barrier per query)
-      const float hm = max_over_q4(lmax);
-      if (q4 == 0) sm.hmax[kd][head] = hm;
-      lds_barrier();
-      // Never lowers the reference: after a restart this tile is replayed and
-      // the raised value must survive, or the restart would repeat.
-      m_ref = fmaxf(m_ref, fmaxf(sm.hmax[0][head], sm.hmax[1][head]));
-    } else if (__ballot(lmax > m_ref + kRefLog2) != 0) {
-      if (max_over_q4(lmax) > m_ref + kRefLog2) sm.restart = 1;
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;  // before the first valid tile: P = 0
-    float pv[4];
+      for (int r = 0; r < 4; ++r) {
+        const int gs = first_tile * kTile + 16 * s + 4 * q4 + r;
+        vmask |= (uint32_t)(gs < top_k && slot_valid(idx_row[gs], p)) << r;
+      }
+      lds_barrier();  // P1: the tile is in stage 0
+      f32x4 sacc[2];
+      qk(sacc, stage0_lds);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(sv[r] - m_use);
-    l_part += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    {
-      const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
-      const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
-      const int poff = p_off(head, 2 * kd + (q4 >> 1)) + 8 * (q4 & 1);  // slots 16 kd + 4 q4 .. +3
-      *reinterpret_cast<u32x2*>(sm.pbuf[0] + poff) = u32x2{h0, h1};
-      if (hilo) {
-        const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
-        const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
-        *reinterpret_cast<u32x2*>(sm.pbuf[1] + poff) = u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)};
+      for (int hb = 0; hb < 2; ++hb) {
+        float lm = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((vmask >> r) & 1u) lm = fmaxf(lm, sacc[hb][r] * scale_log2);
+        const float hm = max_over_q4(lm);
+        if (q4 == 0) sm.hmax[1][s][head[hb]] = hm;  // parity 1: tile 0 writes parity 0 while these are read
+      }
+      lds_barrier();  // P2: both halves' maxima published; stage 0 free
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(sm.hmax[1][0][head[hb]], sm.hmax[1][1][head[hb]]);
+    }
+
+    int st = 0;  // stage of tile t
+    for (int t = 0; t <= n_tiles; ++t) {
+      lds_barrier();  // B(t): tile t resident; P(t - 1) complete
+      // The flags, maxima and P buffers alternate by tile parity: a wave that
+      // is already scoring tile t writes the other parity than the one the
+      // slower waves still read for tile t - 1.
+      if (sm.restart[(t - 1) & 1]) {  // raised while scoring tile t - 1 (block-uniform; rare)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          m_ref[hb] = fmaxf(m_ref[hb], fmaxf(sm.hmax[(t - 1) & 1][0][head[hb]], sm.hmax[(t - 1) & 1][1][head[hb]]));
+          l_part[hb] = 0.0f;
+        }
+        --restarts_left;
+        lds_barrier();  // R1: flag and maxima read everywhere
+        if (tid == 0) sm.restart[(t - 1) & 1] = 0;
+        lds_barrier();  // R2: ring refilled, flag cleared
+        t = -1;
+        st = 0;
+        continue;
+      }
+      if (t < n_tiles) {
+        f32x4 sacc[2];
+        qk(sacc, stage0_lds + kStageBytes * st);
+        const u32x4 jv = *reinterpret_cast<const u32x4*>(&sm.ring[t % kRingTiles][16 * s + 4 * q4]);
+        uint32_t vmask = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gs = t * kTile + 16 * s + 4 * q4 + r;
+          vmask |= (uint32_t)(gs < top_k && slot_valid((int32_t)jv[r], p)) << r;
+        }
+        bool over = false;
+        uint8_t* pb = sm.pbuf[t & 1];
+        uint8_t* pl = sm.stage[kStages - 1] + (t & 1) * (kH * kTile * 2);  // lo part (hi/lo queries)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          float sv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv[r] = ((vmask >> r) & 1u) ? sacc[hb][r] * scale_log2 : -INFINITY;
+          const float lm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          over |= lm > m_ref[hb] + kRefLog2;
+          const float hm = max_over_q4(lm);
+          if (q4 == 0) sm.hmax[t & 1][s][head[hb]] = hm;
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(sv[r] - m_ref[hb]);
+          l_part[hb] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+          const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
+          const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
+          *reinterpret_cast<u32x2*>(pb + poff[hb]) = u32x2{h0, h1};
+          if (HILO) {
+            const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
+            const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
+            *reinterpret_cast<u32x2*>(pl + poff[hb]) = u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)};
+          }
+        }
+        if (__ballot(over) != 0 && restarts_left > 0) sm.restart[t & 1] = 1;
+      }
+      st = (st + 1 == S) ? 0 : st + 1;
+    }
+    // ---- epilogue: denominators to the P V waves; lse = (m + log2 l) * ln 2.
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float lh = sum_over_q4(l_part[hb]);
+      if (q4 == 0) sm.lsum[s][head[hb]] = lh;
+    }
+    __syncthreads();  // E1
+    if (lse && s == 0 && q4 == 0) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float l_run = sm.lsum[0][head[hb]] + sm.lsum[1][head[hb]];
+        lse[(int64_t)i * kH + head[hb]] =
+            (l_run > 0.0f) ? (m_ref[hb] + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f : -INFINITY;
       }
     }
-    lds_barrier();
+  };
 
-    if (sm.restart && restarts_left > 0) {  // block-uniform (written before the barrier above); rare
-      --restarts_left;
-      const float hm = max_over_q4(lmax);
-      if (q4 == 0) sm.hmax[kd][head] = hm;
-      wait_vmcnt<0>();  // drain the loads of later tiles
+  // ======================================================= gather / P V waves
+  auto pv_role = [&](auto hilo_c) {
+    constexpr bool HILO = decltype(hilo_c)::value;
+    constexpr int S = HILO ? kStages - 1 : kStages;
+    constexpr int kAhead = S - 2;  // tiles loaded ahead of the score waves' tile
+    const int v = wave - 4;
+    const uint8_t* __restrict__ kvb = reinterpret_cast<const uint8_t*>(kv);
+    const uint32_t lane16 = 16u * (uint32_t)lane;
+    const uint32_t rope_lane = 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swr(8 * v + (lane >> 3)));
+    const int gslot = 8 * v + (lane >> 3);  // this lane's slot for the gather row offsets
+    // Transposed V reads (B operand): lane 16G + 4e + c addresses row
+    // 8G + 4h + e, dims 128v + 16nb + 4c .. +3 (piece 16v + 2nb + c/2, byte
+    // 8 (c % 2) inside it); entry x = 2 nb + h.
+    uint32_t tr_base[16];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
-      l_part = 0.0f;
-      lds_barrier();  // flag read everywhere, maxima published; nobody reads a stage or P now
-      m_ref = fmaxf(m_ref, fmaxf(sm.hmax[0][head], sm.hmax[1][head]));
-      if (tid == 0) sm.restart = 0;
-      issue_tile(sm, kvb, 0, 0, wave, lane, p32);
-      if (n_tiles > 1) issue_tile(sm, kvb, 1, 1, wave, lane, p32);
-      t = -1;
-      st = kStages - 1;  // the loop increment brings it to stage 0 with t = 0
-      continue;
+    for (int x = 0; x < 16; ++x) {
+      const int nb = x >> 1, h = x & 1, e = l16 >> 2, c = l16 & 3;
+      tr_base[x] = lat_off(8 * q4 + 4 * h + e, 16 * v + 2 * nb + (c >> 1)) + 8 * (c & 1);
     }
-    // ---- O[64 heads][dims 64w..] += P V, V read straight from the tile's
-    // latent part through transposed LDS reads.
-    const uint32_t tile_lds = lds_addr(tileb);
-    if (hilo) pv_tile<true>(o, sm, tile_lds, tr_base, l16, q4);
-    else pv_tile<false>(o, sm, tile_lds, tr_base, l16, q4);
-  }
+    f32x4 o[4][8];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
 
-  // ---- epilogue: O / l, lse = (m + log2 l) * ln 2.
-  const float lh = sum_over_q4(l_part);
-  if (q4 == 0) sm.hsum[kd][head] = lh;
-  __syncthreads();
-  if (wave < 4 && q4 == 0) {
-    const float l_run = sm.hsum[0][head] + sm.hsum[1][head];
-    if (lse) lse[(int64_t)i * kH + head] = (l_run > 0.0f) ? (m_ref + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f : -INFINITY;
-  }
-  float* __restrict__ orow = out + (int64_t)i * kH * kDL;
+    auto pv = [&](uint32_t tile_lds, int par) {
+      const uint32_t pbase[2] = {lds_addr(sm.pbuf[par]), lds_addr(sm.stage[kStages - 1]) + par * (kH * kTile * 2)};
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    float f[4];
+      for (int part = 0; part < (HILO ? 2 : 1); ++part) {
+        bf16x8 pa[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hh = 16 * mb + 4 * q4 + r;
-      const float l_run = sm.hsum[0][hh] + sm.hsum[1][hh];
-      f[r] = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+        for (int mb = 0; mb < 4; ++mb) pa[mb] = __builtin_bit_cast(bf16x8, lds_read16(pbase[part] + p_off(16 * mb + l16, q4)));
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const s16x4 d0 = lds_read_tr(tile_lds + tr_base[2 * nb]);
+          const s16x4 d1 = lds_read_tr(tile_lds + tr_base[2 * nb + 1]);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, (s16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]}));
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], vf, o[mb][nb], 0, 0, 0);
+        }
+      }
+    };
+    auto ring_roff = [&](int tile) {
+      return row_off(sm.ring[tile % kRingTiles][gslot], tile * kTile + gslot, top_k, p32);
+    };
+    auto start_pipeline = [&]() {
+#pragma unroll
+      for (int a = 0; a < kAhead; ++a)
+        if (a < n_tiles) gather_tile(kvb, ring_roff(a), stage0_lds + kStageBytes * a, v, lane16, rope_lane);
+    };
+
+    if (n_tiles > 0) {  // reference prologue: the first tile with a valid slot into stage 0
+      const int gs = first_tile * kTile + gslot;
+      gather_tile(kvb, row_off(gs < top_k ? idx_row[gs] : -1, gs, top_k, p32), stage0_lds, v, lane16, rope_lane);
+      wait_vmcnt<0>();
+      lds_barrier();  // P1
+      lds_barrier();  // P2: the score waves are done with stage 0
     }
+    start_pipeline();
+    int st = 0;  // stage of tile t
+    for (int t = 0; t <= n_tiles; ++t) {
+      // Wait for this wave's loads of tile t; tile t + 1's (and a ring refill
+      // issued in iteration t - 1) may stay in flight.
+      if (t < n_tiles) {
+        if (HILO) {
+          wait_vmcnt<0>();
+        } else {
+          const bool next_out = t + 1 < n_tiles;
+          const bool ring_out = wave == 7 && ((t - 1) % 8 == 0) && t - 1 >= 8 && 8 * ((t - 1) / 8 + 1) < n_tiles;
+          if (next_out) {
+            if (ring_out) wait_vmcnt<kGatherLoads + 1>();
+            else wait_vmcnt<kGatherLoads>();
+          } else {
+            if (ring_out) wait_vmcnt<1>();
+            else wait_vmcnt<0>();
+          }
+        }
+      }
+      lds_barrier();  // B(t)
+      if (sm.restart[(t - 1) & 1]) {
+        wait_vmcnt<0>();  // drain the loads of later tiles
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        orow[(int64_t)(16 * mb + 4 * q4 + r) * kDL + 64 * wave + 16 * nb + l16] = o[mb][nb][r] * f[r];
+          for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
+        --restarts_left;
+        lds_barrier();  // R1: no stage, P or ring read in flight
+        if (wave == 7) {
+          issue_ring(sm, idx_row, 0, top_k, lane);
+          issue_ring(sm, idx_row, 1, top_k, lane);
+          wait_vmcnt<0>();
+        }
+        lds_barrier();  // R2
+        start_pipeline();
+        t = -1;
+        st = 0;
+        continue;
+      }
+      if (wave == 7 && (t % 8 == 0) && t >= 8 && 8 * (t / 8 + 1) < n_tiles) issue_ring(sm, idx_row, t / 8 + 1, top_k, lane);
+      const int t_next = t + kAhead;
+      if (t_next < n_tiles) {
+        int sn = st + kAhead;
+        if (sn >= S) sn -= S;
+        gather_tile(kvb, ring_roff(t_next), stage0_lds + kStageBytes * sn, v, lane16, rope_lane);
+      }
+      if (t > 0) pv(stage0_lds + kStageBytes * (st == 0 ? S - 1 : st - 1), (t - 1) & 1);
+      st = (st + 1 == S) ? 0 : st + 1;
+    }
+    // ---- epilogue: O / l.
+    __syncthreads();  // E1: denominators published
+    float* __restrict__ orow = out + (int64_t)i * kH * kDL + 128 * v + l16;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      float f[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = 16 * mb + 4 * q4 + r;
+        const float l_run = sm.lsum[0][hh] + sm.lsum[1][hh];
+        f[r] = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_nontemporal_store(o[mb][nb][r] * f[r], orow + (int64_t)(16 * mb + 4 * q4 + r) * kDL + 16 * nb);
+    }
+  };
+
+  if (wave < 4) {
+    if (hilo) score_role(std::true_type{});
+    else score_role(std::false_type{});
+  } else {
+    if (hilo) pv_role(std::true_type{});
+    else pv_role(std::false_type{});
   }
 }
 
 }  // namespace
 
 bool mla_fast_path(const MlaArgs& a) {
-  return a.bf16 && a.n_heads == kH && a.d_latent == kDL && a.d_rope == kDR && a.top_k <= kMaxTopk;
+  // top_k % 4 == 0: the index ring is filled with 16-byte loads from 16-byte aligned rows.
+  // The cache must stay below 4 GiB (32-bit byte offsets).
+  return a.bf16 && a.n_heads == kH && a.d_latent == kDL && a.d_rope == kDR && a.top_k % 4 == 0 &&
+         (int64_t)(a.offset + a.n_q) * kRowBytes < ((int64_t)1 << 32);
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {

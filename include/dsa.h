@@ -143,7 +143,10 @@ DSA_API dsa_status dsa_topk_select(const dsa_dims *dims, const float *scores, in
  *   lse       [n_q][n_heads] fp32, or NULL when not wanted
  * bf16 inputs are multiplied on the matrix cores with fp32 accumulation and an
  * fp32 softmax. Fast path: bf16 with n_heads == 64, d_latent == 512,
- * d_rope == 64; every other shape runs a plain kernel (fp32 math).
+ * d_rope == 64, top_k a multiple of 4 (1 <= top_k <= 2^20) and a cache of
+ * less than 4 GiB ((offset + n_q) * 1152 bytes); every other shape runs a
+ * plain kernel (fp32 math, d_latent + d_rope <= 2048, top_k <= 4096, else
+ * DSA_ERR_UNSUPPORTED).
  */
 DSA_API dsa_status dsa_sparse_mla_fwd(const dsa_dims *dims, const void *q, const void *kv_cache,
                               const int32_t *idx, float *out, float *lse, void *stream);
