@@ -130,14 +130,13 @@ constexpr int kDL = 512;            // latent / value dims
 constexpr int kDR = 64;             // rope dims
 constexpr int kDQK = kDL + kDR;     // 576
 constexpr int kTile = 32;           // selected slots per tile
-constexpr int kThreads = 512;       // 8 waves: 4 score waves + 4 gather / P V waves
+constexpr int kThreads = 512;       // 8 waves: 4 score waves + 4 P V waves
 constexpr int kStages = 4;          // LDS tile stages (hi/lo queries use 3; P's lo part takes the 4th)
 constexpr int kRowBytes = kDQK * 2;              // 1152 = 72 pieces of 16 bytes
 constexpr int kStageBytes = kTile * kRowBytes;   // 36 KB
 constexpr int kRingTiles = 24;      // index ring: 3 parts of 8 tiles (1 KB each)
 constexpr int kHiloMaxValid = 512;  // queries with at most this many valid keys use hi/lo P
 constexpr float kRefLog2 = 64.0f;   // P = exp2(s - m_ref) < 2^64 before a restart is forced
-constexpr int kGatherLoads = 9;     // loads per tile and gather wave: 8 latent rows + one rope block
 
 // Max / sum over the four lanes l16 + 16*q (q = 0..3) that hold one head, with
 // the gfx950 VALU lane swaps (xor-32, then xor-16 within each half).
@@ -167,9 +166,9 @@ struct MlaSmem {
   uint8_t stage[kStages][kStageBytes];  // tiles: [32 rows][1 KB latent] then [32 rows][128 B rope]
   uint8_t pbuf[2][kH * kTile * 2];      // P hi part (bf16, chunk-swizzled rows) by tile parity
   int32_t ring[kRingTiles][kTile];      // the query's index row, tile t at t % 24
-  float hmax[2][2][kH];                 // [tile parity][slot half][head]: the head's max over that half
+  float hmax[2][kH];                    // [slot half][head]: maxima exchanged between the slot halves
   float lsum[2][kH];                    // [slot half][head]: softmax denominators at the end
-  int32_t restart[2];                   // [tile parity]: a head needs a higher reference, restart
+  int32_t restart;                      // a head passed its reference by more than kRefLog2
   int32_t c_last, c_valid, c_first;     // index row census
 };
 
@@ -218,6 +217,9 @@ typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 __device__ __forceinline__ u32x4 lds_read16(uint32_t a) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((lds_u8*)(uintptr_t)a);
 }
+__device__ __forceinline__ void lds_write8(uint32_t a, u32x2 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((__attribute__((address_space(3))) uint8_t*)(uintptr_t)a) = v;
+}
 __device__ __forceinline__ s16x4 lds_read_tr(uint32_t a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u8*)(uintptr_t)a));
 }
@@ -231,7 +233,7 @@ __device__ __forceinline__ s16x4 lds_read_tr(uint32_t a) {
 __device__ __forceinline__ void dma16(const void* __restrict__ base, uint32_t off, uint32_t lds) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds));
 #pragma clang diagnostic pop
 }
 
@@ -243,20 +245,35 @@ __device__ __forceinline__ uint32_t row_off(int32_t j, int slot, int top_k, uint
   return ((slot < top_k && j >= 0 && (uint32_t)j <= p) ? (uint32_t)j : p) * (uint32_t)kRowBytes;
 }
 
-// Gather of one tile by gather wave v (slots 8v .. 8v+7): the latent parts of
-// its 8 rows (1 KB each; lane L fills position L of row m = 8v + u, i.e. loads
-// piece L ^ swl(m)) and their rope parts (one 1 KB load; lane L fills position
-// L % 8 of row 8v + L / 8, i.e. loads rope piece (L % 8) ^ swr(row)). `roff` is
-// lane L's row offset for slot 8v + L / 8.
-__device__ __forceinline__ void gather_tile(const uint8_t* __restrict__ kv, uint32_t roff, uint32_t stage_lds, int v,
-                                            uint32_t lane16, uint32_t rope_lane) {
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int m = 8 * v + u;
-    const uint32_t row = __builtin_amdgcn_readlane(roff, 8 * u);  // wave-uniform
+// Tile loads, spread over all 8 waves: wave w loads the latent parts of the
+// rows of slots 4w .. 4w+3 (one 1 KB load each; lane L fills position L of row
+// m, i.e. loads piece L ^ swl(m)), and waves 0-3 also the rope parts of rows
+// 8w .. 8w+7 (one 1 KB load; lane L fills position L % 8 of row 8w + L / 8,
+// i.e. loads rope piece (L % 8) ^ swr(row)). Per tile: 5 loads for waves 0-3,
+// 4 for waves 4-7.
+struct GatherRows {
+  uint32_t lat;   // row offset of slot lane % 32 (taken per load with readlane)
+  uint32_t rope;  // row offset of slot 8w + lane / 8 (waves 0-3)
+};
+__device__ __forceinline__ GatherRows gather_rows(const int32_t* ring_tile, int tile, int wave, int lane, int top_k,
+                                                  uint32_t p) {
+  const int sl = lane & 31, sr = 8 * (wave & 3) + (lane >> 3);
+  GatherRows g;
+  g.lat = row_off(ring_tile[sl], tile * kTile + sl, top_k, p);
+  g.rope = row_off(ring_tile[sr], tile * kTile + sr, top_k, p);
+  return g;
+}
+// Load u of a tile for wave w: u < 4 latent block 4w + u; u = 4 the rope
+// block (waves 0-3 only: the caller knows its role).
+__device__ __forceinline__ void gather_load(const uint8_t* __restrict__ kv, const GatherRows& g, uint32_t stage_lds,
+                                            uint32_t lane16, uint32_t rope_lane, int u, int wave) {
+  if (u < 4) {
+    const int m = 4 * wave + u;
+    const uint32_t row = __builtin_amdgcn_readlane(g.lat, m);  // wave-uniform
     dma16(kv + row, lane16 ^ (uint32_t)(16 * (m & 15)), stage_lds + kLatBytes * m);
+  } else {
+    dma16(kv, g.rope + rope_lane, stage_lds + kRopeOff + 1024 * wave);
   }
-  dma16(kv, roff + rope_lane, stage_lds + kRopeOff + 1024 * v);
 }
 
 // Index ring refill: tiles 8c .. 8c+7 of the index row (1 KB) into ring part
@@ -275,17 +292,19 @@ __device__ __forceinline__ void issue_ring(MlaSmem& sm, const int32_t* __restric
 //     32 g .. +31 and slots 16 s .. +15 of a tile over all 576 dims (the
 //     query's Q fragments for those heads stay in registers), then the
 //     softmax of those scores; P goes to LDS as bf16;
-//   gather / P V waves (w = 4..7; v = w - 4): the direct-to-LDS loads of
-//     slots 8v .. 8v+7 of the tiles two ahead, and O += P V for output dims
-//     128 v .. +127 of all 64 heads.
-// In iteration t the score waves work on tile t while the P V waves work on
-// tile t - 1; tiles t + 1 and t + 2 are in flight (4 stages).
+//   P V waves (w = 4..7; v = w - 4): O += P V for output dims 128 v .. +127
+//     of all 64 heads.
+// All waves share the direct-to-LDS tile loads, issued between their MFMAs.
+// In iteration t the score waves work on tile t and the P V waves on tile
+// t - 1, while tiles t + 1 and t + 2 are loading (4 stages).
 //
 // The softmax needs no running rescale: every head gets a fixed reference
-// m_ref (log2 domain), its maximum over the first tile with a valid slot, and
-// P = exp2(s - m_ref) stays below 2^kRefLog2 until a logit exceeds
-// m_ref + kRefLog2; then the query restarts from tile 0 with the reference
-// raised to that tile's maximum (a later tile each time, so it ends).
+// m_ref (log2 domain), its maximum over the first tile with a valid slot
+// (the two slot halves agree on it through LDS in that iteration), and
+// P = exp2(s - m_ref). The score waves track the largest s - m_ref; if a
+// head's passed kRefLog2 (P could leave the range in which the fp32 sums
+// stay accurate), the query is computed once more with each head's
+// reference raised to its maximum.
 __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offset, int top_k, float scale_log2,
                                                                const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ kv,
@@ -293,30 +312,43 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
                                                                float* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) MlaSmem sm;
   const int i = n_q - 1 - (int)blockIdx.x;  // latest queries (most keys) first
-  const int64_t p = (int64_t)offset + i;
-  const uint32_t p32 = (uint32_t)p;
+  const uint32_t p32 = (uint32_t)(offset + i);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
   const int32_t* __restrict__ idx_row = idx + (int64_t)i * top_k;
+  const uint8_t* __restrict__ kvb = reinterpret_cast<const uint8_t*>(kv);
+  const uint32_t stage0_lds = lds_addr(sm.stage[0]);
+  const uint32_t pbuf_lds = lds_addr(sm.pbuf[0]);
+  const uint32_t plo_lds = lds_addr(sm.stage[kStages - 1]);  // P lo parts (hi/lo queries)
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  const uint32_t rope_lane = 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swr(8 * (wave & 3) + (lane >> 3)));
 
-  // ---- census of the index row: valid slots, last valid slot, first valid tile.
   if (tid == 0) {
     sm.c_last = 0;
     sm.c_valid = 0;
     sm.c_first = 0x7fffffff;
-    sm.restart[0] = 0;
-    sm.restart[1] = 0;
+    sm.restart = 0;
   }
   __syncthreads();
-  {
+
+  // Census of the index row (valid slots, last valid slot, first tile with a
+  // valid slot), then the tile range. Called by both roles after they have
+  // issued their own first loads, so that the latencies overlap.
+  int n_tiles = 0, first_tile = 0, t0 = 0;
+  bool hilo = false;
+  auto census = [&]() {
     int last = 0, cnt = 0, first = 0x7fffffff;
-    for (int t = tid; t < top_k; t += kThreads) {
-      if (slot_valid(idx_row[t], p)) {
-        last = t + 1;
-        first = min(first, t / kTile);
-        ++cnt;
+    for (int b = 4 * tid; b < top_k; b += 4 * kThreads) {  // top_k % 4 == 0: 16-byte reads
+      const u32x4 j4 = *reinterpret_cast<const u32x4*>(idx_row + b);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (j4[r] <= p32) {  // 0 <= j <= p (negative j compare as large)
+          last = b + r + 1;
+          first = min(first, (b + r) / kTile);
+          ++cnt;
+        }
       }
     }
     last = wave_max_int(last);
@@ -327,41 +359,74 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
       atomicAdd(&sm.c_valid, cnt);
       atomicMin(&sm.c_first, first);
     }
-  }
-  if (wave == 7) {  // index ring: tiles 0..15
-    issue_ring(sm, idx_row, 0, top_k, lane);
-    issue_ring(sm, idx_row, 1, top_k, lane);
-  }
-  // Every load above completes here: inside the tile loop the only
-  // vector-memory operations are the tile and ring loads, whose counts the
-  // explicit vmcnt waits rely on.
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // census and ring visible
-  const int n_tiles = (sm.c_last + kTile - 1) / kTile;
-  const int first_tile = sm.c_first;
-  const bool hilo = sm.c_valid <= kHiloMaxValid;
-  const uint32_t stage0_lds = lds_addr(sm.stage[0]);
-  int restarts_left = n_tiles;
+    if (wave == 7) {  // index ring, tiles 0..15 (reloaded below if the first valid tile lies further)
+      issue_ring(sm, idx_row, 0, top_k, lane);
+      issue_ring(sm, idx_row, 1, top_k, lane);
+    }
+    // Every load so far completes here: inside the tile loop the only
+    // vector-memory operations are the tile and ring loads, whose counts the
+    // explicit vmcnt waits rely on.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    n_tiles = (sm.c_last + kTile - 1) / kTile;
+    first_tile = n_tiles > 0 ? sm.c_first : 0;
+    t0 = first_tile & ~7;  // the loop starts at a ring chunk boundary
+    hilo = sm.c_valid <= kHiloMaxValid;
+    if (t0 != 0) {  // rare: no valid slot in tiles 0..7
+      if (wave == 7) {
+        issue_ring(sm, idx_row, t0 / 8, top_k, lane);
+        issue_ring(sm, idx_row, t0 / 8 + 1, top_k, lane);
+        wait_vmcnt<0>();
+      }
+      __syncthreads();
+    }
+  };
+
+  // Waits, before the barrier of iteration t, for this wave's loads of tile
+  // t: the loads of tile t + 1 and a ring refill issued in iteration t - 1
+  // (wave 7) may stay in flight.
+  auto wait_tile = [&](int t, auto hilo_c) {
+    constexpr bool HILO = decltype(hilo_c)::value;
+    if (t >= n_tiles) return;
+    if (HILO) {  // tile t + 1 is issued after this barrier
+      wait_vmcnt<0>();
+      return;
+    }
+    const bool next_out = t + 1 < n_tiles;
+    const bool ring_out = wave == 7 && ((t - 1) & 7) == 0 && t - 1 >= t0 + 8 && 8 * ((t - 1) / 8 + 1) < n_tiles;
+    if (wave < 4) {
+      if (next_out) wait_vmcnt<5>();
+      else wait_vmcnt<0>();
+    } else if (next_out) {
+      if (ring_out) wait_vmcnt<5>();
+      else wait_vmcnt<4>();
+    } else {
+      if (ring_out) wait_vmcnt<1>();
+      else wait_vmcnt<0>();
+    }
+  };
+  auto issue_all = [&](const GatherRows& g, uint32_t stage_lds) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gather_load(kvb, g, stage_lds, lane16, rope_lane, u, wave);
+    if (wave < 4) gather_load(kvb, g, stage_lds, lane16, rope_lane, 4, wave);
+  };
+  auto start_pipeline = [&](int ahead) {
+    for (int a = 0; a < ahead; ++a)
+      if (t0 + a < n_tiles)
+        issue_all(gather_rows(sm.ring[(t0 + a) % kRingTiles], t0 + a, wave, lane, top_k, p32),
+                  stage0_lds + kStageBytes * a);
+  };
 
   // ================================================================ score waves
-  auto score_role = [&](auto hilo_c) {
+  auto score_role = [&](auto hilo_c, const bf16x8 (&qf)[2][18]) {
     constexpr bool HILO = decltype(hilo_c)::value;
     constexpr int S = HILO ? kStages - 1 : kStages;
+    constexpr int kAhead = S - 2;
     const int g = wave & 1, s = wave >> 1;
     int head[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) head[hb] = 32 * g + 16 * hb + l16;
-    // Q fragments (B operand): head[hb], k-step u covers dims 32u + 8 q4 .. +7.
-    bf16x8 qf[2][18];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const uint16_t* qsrc = q + ((int64_t)i * kH + head[hb]) * kDQK + 8 * q4;
-#pragma unroll
-      for (int u = 0; u < 18; ++u) qf[hb][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 32 * u));
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0);
     // K operand (A): row 16 s + l16 of the tile, piece 4u + q4. For u < 16 the
     // swizzle keeps the piece inside its group of 16, so the offset is
     // qk_lat[u % 4] + 256 (u / 4); the rope k-steps u = 16, 17 have their own.
@@ -372,105 +437,115 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 #pragma unroll
     for (int x = 0; x < 2; ++x) qk_rope[x] = rope_off(krow, 4 * x + q4);
     // P write position of this lane's 4 slots 16 s + 4 q4 .. +3 in each head row.
-    int poff[2];
+    uint32_t poff[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) poff[hb] = p_off(head[hb], 2 * s + (q4 >> 1)) + 8 * (q4 & 1);
 
-    auto qk = [&](f32x4 (&sacc)[2], uint32_t tile_lds) {
-      sacc[0] = f32x4{0, 0, 0, 0};
-      sacc[1] = f32x4{0, 0, 0, 0};
+    float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.0f, 0.0f}, runmax[2] = {-INFINITY, -INFINITY};
+
+    auto pass = [&](const bf16x8 (&qf)[2][18], bool first_pass) {
+      start_pipeline(kAhead);
+      int st = 0;  // stage of tile t
+      for (int t = t0; t <= n_tiles; ++t) {
+        wait_tile(t, hilo_c);
+        lds_barrier();  // B(t): tile t resident; P(t - 1) complete
+        const int t_next = t + kAhead;
+        const bool more = t_next < n_tiles;
+        int sn = st + kAhead;
+        if (sn >= S) sn -= S;
+        const uint32_t next_lds = stage0_lds + kStageBytes * sn;
+        const GatherRows rows = gather_rows(sm.ring[(more ? t_next : t0) % kRingTiles], t_next, wave, lane, top_k, p32);
+        if (t < n_tiles && t >= first_tile) {
+          // ---- S^T = K Q^T; tile t + kAhead's loads go out between the MFMAs
+          const uint32_t tile_lds = stage0_lds + kStageBytes * st;
+          uint32_t kb[6];
 #pragma unroll
-      for (int u = 0; u < 18; ++u) {
-        const uint32_t a = tile_lds + (u < 16 ? qk_lat[u & 3] + 256 * (u >> 2) : qk_rope[u - 16]);
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, lds_read16(a));
+          for (int x = 0; x < 4; ++x) kb[x] = tile_lds + qk_lat[x];
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[hb][u], sacc[hb], 0, 0, 0);
+          for (int x = 0; x < 2; ++x) kb[4 + x] = tile_lds + qk_rope[x];
+          // The operand reads run three k-steps ahead (written out, since the
+          // load branches split the sequence into blocks the scheduler cannot
+          // move reads across).
+          auto kread = [&](int u) {
+            return __builtin_bit_cast(bf16x8, lds_read16((u < 16) ? kb[u & 3] + 256 * (u >> 2) : kb[4 + (u - 16)]));
+          };
+          f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+          bf16x8 kf[3] = {kread(0), kread(1), kread(2)};
+#pragma unroll
+          for (int u = 0; u < 18; ++u) {
+            const bf16x8 cur = kf[u % 3];
+            if (u + 3 < 18) kf[u % 3] = kread(u + 3);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+              sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[hb][u], sacc[hb], 0, 0, 0);
+            if (more && u % 3 == 1 && u / 3 < 5) gather_load(kvb, rows, next_lds, lane16, rope_lane, u / 3, wave);
+          }
+          // ---- slot validity (from the ring)
+          const u32x4 jv = *reinterpret_cast<const u32x4*>(&sm.ring[t % kRingTiles][16 * s + 4 * q4]);
+          const int gs0 = t * kTile + 16 * s + 4 * q4;
+          bool vm[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vm[r] = gs0 + r < top_k && jv[r] <= p32;
+          if (first_pass && t == first_tile) {  // reference: the head's max over this tile
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              float lm = -INFINITY;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (vm[r]) lm = fmaxf(lm, sacc[hb][r] * scale_log2);
+              const float hm = max_over_q4(lm);
+              if (q4 == 0) sm.hmax[s][head[hb]] = hm;
+            }
+            lds_barrier();  // X: both slot halves' maxima published
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(sm.hmax[0][head[hb]], sm.hmax[1][head[hb]]);
+          }
+          // ---- softmax numerators P = exp2(s * scale - m_ref), bf16 to LDS (the
+          // product is rounded as in the reference, so its maximum gets P = 1 exactly)
+          const uint32_t par = (uint32_t)(t & 1) * (kH * kTile * 2);
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = vm[r] ? sacc[hb][r] * scale_log2 - m_ref[hb] : -INFINITY;
+            runmax[hb] = fmaxf(runmax[hb], fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+            float pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(x[r]);
+            l_part[hb] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+            const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
+            const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
+            lds_write8(pbuf_lds + par + poff[hb], u32x2{h0, h1});
+            if (HILO) {
+              const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
+              const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
+              lds_write8(plo_lds + par + poff[hb], u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)});
+            }
+          }
+        } else if (more) {
+          issue_all(rows, next_lds);
+        }
+        st = (st + 1 == S) ? 0 : st + 1;
       }
     };
 
-    float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.0f, 0.0f};
-    if (n_tiles > 0) {  // reference prologue on the first tile with a valid slot
-      uint32_t vmask = 0;
+    pass(qf, true);
+    // ---- did a head's scores pass its reference by more than kRefLog2?
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gs = first_tile * kTile + 16 * s + 4 * q4 + r;
-        vmask |= (uint32_t)(gs < top_k && slot_valid(idx_row[gs], p)) << r;
-      }
-      lds_barrier();  // P1: the tile is in stage 0
-      f32x4 sacc[2];
-      qk(sacc, stage0_lds);
+    for (int hb = 0; hb < 2; ++hb) {
+      const float hm = max_over_q4(runmax[hb]);
+      if (q4 == 0) sm.hmax[s][head[hb]] = hm;
+    }
+    if (__ballot(runmax[0] > kRefLog2 || runmax[1] > kRefLog2) != 0) sm.restart = 1;
+    lds_barrier();  // Z
+    if (sm.restart) {  // block-uniform; rare
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        float lm = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if ((vmask >> r) & 1u) lm = fmaxf(lm, sacc[hb][r] * scale_log2);
-        const float hm = max_over_q4(lm);
-        if (q4 == 0) sm.hmax[1][s][head[hb]] = hm;  // parity 1: tile 0 writes parity 0 while these are read
+        m_ref[hb] += fmaxf(sm.hmax[0][head[hb]], sm.hmax[1][head[hb]]);
+        l_part[hb] = 0.0f;
       }
-      lds_barrier();  // P2: both halves' maxima published; stage 0 free
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(sm.hmax[1][0][head[hb]], sm.hmax[1][1][head[hb]]);
-    }
-
-    int st = 0;  // stage of tile t
-    for (int t = 0; t <= n_tiles; ++t) {
-      lds_barrier();  // B(t): tile t resident; P(t - 1) complete
-      // The flags, maxima and P buffers alternate by tile parity: a wave that
-      // is already scoring tile t writes the other parity than the one the
-      // slower waves still read for tile t - 1.
-      if (sm.restart[(t - 1) & 1]) {  // raised while scoring tile t - 1 (block-uniform; rare)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          m_ref[hb] = fmaxf(m_ref[hb], fmaxf(sm.hmax[(t - 1) & 1][0][head[hb]], sm.hmax[(t - 1) & 1][1][head[hb]]));
-          l_part[hb] = 0.0f;
-        }
-        --restarts_left;
-        lds_barrier();  // R1: flag and maxima read everywhere
-        if (tid == 0) sm.restart[(t - 1) & 1] = 0;
-        lds_barrier();  // R2: ring refilled, flag cleared
-        t = -1;
-        st = 0;
-        continue;
-      }
-      if (t < n_tiles) {
-        f32x4 sacc[2];
-        qk(sacc, stage0_lds + kStageBytes * st);
-        const u32x4 jv = *reinterpret_cast<const u32x4*>(&sm.ring[t % kRingTiles][16 * s + 4 * q4]);
-        uint32_t vmask = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gs = t * kTile + 16 * s + 4 * q4 + r;
-          vmask |= (uint32_t)(gs < top_k && slot_valid((int32_t)jv[r], p)) << r;
-        }
-        bool over = false;
-        uint8_t* pb = sm.pbuf[t & 1];
-        uint8_t* pl = sm.stage[kStages - 1] + (t & 1) * (kH * kTile * 2);  // lo part (hi/lo queries)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          float sv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sv[r] = ((vmask >> r) & 1u) ? sacc[hb][r] * scale_log2 : -INFINITY;
-          const float lm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-          over |= lm > m_ref[hb] + kRefLog2;
-          const float hm = max_over_q4(lm);
-          if (q4 == 0) sm.hmax[t & 1][s][head[hb]] = hm;
-          float pv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(sv[r] - m_ref[hb]);
-          l_part[hb] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-          const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
-          const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
-          *reinterpret_cast<u32x2*>(pb + poff[hb]) = u32x2{h0, h1};
-          if (HILO) {
-            const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
-            const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
-            *reinterpret_cast<u32x2*>(pl + poff[hb]) = u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)};
-          }
-        }
-        if (__ballot(over) != 0 && restarts_left > 0) sm.restart[t & 1] = 1;
-      }
-      st = (st + 1 == S) ? 0 : st + 1;
+      lds_barrier();  // Z2: ring reloaded
+      pass(qf, false);
     }
     // ---- epilogue: denominators to the P V waves; lse = (m + log2 l) * ln 2.
 #pragma unroll
@@ -489,16 +564,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     }
   };
 
-  // ======================================================= gather / P V waves
+  // ================================================================= P V waves
   auto pv_role = [&](auto hilo_c) {
     constexpr bool HILO = decltype(hilo_c)::value;
     constexpr int S = HILO ? kStages - 1 : kStages;
-    constexpr int kAhead = S - 2;  // tiles loaded ahead of the score waves' tile
+    constexpr int kAhead = S - 2;
     const int v = wave - 4;
-    const uint8_t* __restrict__ kvb = reinterpret_cast<const uint8_t*>(kv);
-    const uint32_t lane16 = 16u * (uint32_t)lane;
-    const uint32_t rope_lane = 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swr(8 * v + (lane >> 3)));
-    const int gslot = 8 * v + (lane >> 3);  // this lane's slot for the gather row offsets
     // Transposed V reads (B operand): lane 16G + 4e + c addresses row
     // 8G + 4h + e, dims 128v + 16nb + 4c .. +3 (piece 16v + 2nb + c/2, byte
     // 8 (c % 2) inside it); entry x = 2 nb + h.
@@ -508,94 +579,78 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
       const int nb = x >> 1, h = x & 1, e = l16 >> 2, c = l16 & 3;
       tr_base[x] = lat_off(8 * q4 + 4 * h + e, 16 * v + 2 * nb + (c >> 1)) + 8 * (c & 1);
     }
+    // P operand (A): head 16 mb + l16, slots 8 q4 .. +7; the head block adds 1 KB.
+    const uint32_t pr = (uint32_t)p_off(l16, q4);
     f32x4 o[4][8];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
 
-    auto pv = [&](uint32_t tile_lds, int par) {
-      const uint32_t pbase[2] = {lds_addr(sm.pbuf[par]), lds_addr(sm.stage[kStages - 1]) + par * (kH * kTile * 2)};
-#pragma unroll
-      for (int part = 0; part < (HILO ? 2 : 1); ++part) {
-        bf16x8 pa[4];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) pa[mb] = __builtin_bit_cast(bf16x8, lds_read16(pbase[part] + p_off(16 * mb + l16, q4)));
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const s16x4 d0 = lds_read_tr(tile_lds + tr_base[2 * nb]);
-          const s16x4 d1 = lds_read_tr(tile_lds + tr_base[2 * nb + 1]);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, (s16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]}));
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], vf, o[mb][nb], 0, 0, 0);
-        }
-      }
-    };
-    auto ring_roff = [&](int tile) {
-      return row_off(sm.ring[tile % kRingTiles][gslot], tile * kTile + gslot, top_k, p32);
-    };
-    auto start_pipeline = [&]() {
-#pragma unroll
-      for (int a = 0; a < kAhead; ++a)
-        if (a < n_tiles) gather_tile(kvb, ring_roff(a), stage0_lds + kStageBytes * a, v, lane16, rope_lane);
-    };
-
-    if (n_tiles > 0) {  // reference prologue: the first tile with a valid slot into stage 0
-      const int gs = first_tile * kTile + gslot;
-      gather_tile(kvb, row_off(gs < top_k ? idx_row[gs] : -1, gs, top_k, p32), stage0_lds, v, lane16, rope_lane);
-      wait_vmcnt<0>();
-      lds_barrier();  // P1
-      lds_barrier();  // P2: the score waves are done with stage 0
-    }
-    start_pipeline();
-    int st = 0;  // stage of tile t
-    for (int t = 0; t <= n_tiles; ++t) {
-      // Wait for this wave's loads of tile t; tile t + 1's (and a ring refill
-      // issued in iteration t - 1) may stay in flight.
-      if (t < n_tiles) {
-        if (HILO) {
-          wait_vmcnt<0>();
-        } else {
-          const bool next_out = t + 1 < n_tiles;
-          const bool ring_out = wave == 7 && ((t - 1) % 8 == 0) && t - 1 >= 8 && 8 * ((t - 1) / 8 + 1) < n_tiles;
-          if (next_out) {
-            if (ring_out) wait_vmcnt<kGatherLoads + 1>();
-            else wait_vmcnt<kGatherLoads>();
-          } else {
-            if (ring_out) wait_vmcnt<1>();
-            else wait_vmcnt<0>();
-          }
-        }
-      }
-      lds_barrier();  // B(t)
-      if (sm.restart[(t - 1) & 1]) {
-        wait_vmcnt<0>();  // drain the loads of later tiles
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
-        --restarts_left;
-        lds_barrier();  // R1: no stage, P or ring read in flight
-        if (wave == 7) {
-          issue_ring(sm, idx_row, 0, top_k, lane);
-          issue_ring(sm, idx_row, 1, top_k, lane);
-          wait_vmcnt<0>();
-        }
-        lds_barrier();  // R2
-        start_pipeline();
-        t = -1;
-        st = 0;
-        continue;
-      }
-      if (wave == 7 && (t % 8 == 0) && t >= 8 && 8 * (t / 8 + 1) < n_tiles) issue_ring(sm, idx_row, t / 8 + 1, top_k, lane);
-      const int t_next = t + kAhead;
-      if (t_next < n_tiles) {
+    auto pass = [&](bool first_pass) {
+      start_pipeline(kAhead);
+      int st = 0;  // stage of tile t
+      for (int t = t0; t <= n_tiles; ++t) {
+        wait_tile(t, hilo_c);
+        lds_barrier();  // B(t)
+        if (wave == 7 && (t & 7) == 0 && t >= t0 + 8 && 8 * (t / 8 + 1) < n_tiles)
+          issue_ring(sm, idx_row, t / 8 + 1, top_k, lane);
+        const int t_next = t + kAhead;
+        const bool more = t_next < n_tiles;
         int sn = st + kAhead;
         if (sn >= S) sn -= S;
-        gather_tile(kvb, ring_roff(t_next), stage0_lds + kStageBytes * sn, v, lane16, rope_lane);
+        const uint32_t next_lds = stage0_lds + kStageBytes * sn;
+        const GatherRows rows = gather_rows(sm.ring[(more ? t_next : t0) % kRingTiles], t_next, wave, lane, top_k, p32);
+        if (t - 1 >= first_tile) {
+          // ---- O += P V for tile t - 1; tile t + kAhead's loads go out between the MFMAs
+          const uint32_t tile_lds = stage0_lds + kStageBytes * (st == 0 ? S - 1 : st - 1);
+          const uint32_t par = (uint32_t)((t - 1) & 1) * (kH * kTile * 2);
+          // V operand reads run two dim blocks ahead (see the score waves).
+          auto vread = [&](int nb) {
+            const s16x4 d0 = lds_read_tr(tile_lds + tr_base[2 * nb]);
+            const s16x4 d1 = lds_read_tr(tile_lds + tr_base[2 * nb + 1]);
+            return __builtin_bit_cast(bf16x8, (s16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]}));
+          };
+#pragma unroll
+          for (int part = 0; part < (HILO ? 2 : 1); ++part) {
+            const uint32_t pb = (part ? plo_lds : pbuf_lds) + par + pr;
+            bf16x8 pa[4];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) pa[mb] = __builtin_bit_cast(bf16x8, lds_read16(pb + 1024 * mb));
+            bf16x8 vf[2] = {vread(0), vread(1)};
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+              const bf16x8 cur = vf[nb & 1];
+              if (nb + 2 < 8) vf[nb & 1] = vread(nb + 2);
+#pragma unroll
+              for (int mb = 0; mb < 4; ++mb)
+                o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], cur, o[mb][nb], 0, 0, 0);
+              if (more && part == 0 && (nb & 1) == 0) gather_load(kvb, rows, next_lds, lane16, rope_lane, nb >> 1, wave);
+            }
+          }
+        } else if (more) {
+          issue_all(rows, next_lds);
+        }
+        // X: the score waves' reference exchange (same condition as theirs)
+        if (first_pass && t == first_tile && t < n_tiles) lds_barrier();
+        st = (st + 1 == S) ? 0 : st + 1;
       }
-      if (t > 0) pv(stage0_lds + kStageBytes * (st == 0 ? S - 1 : st - 1), (t - 1) & 1);
-      st = (st + 1 == S) ? 0 : st + 1;
+    };
+
+    pass(true);
+    lds_barrier();  // Z
+    if (sm.restart) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
+      if (wave == 7) {
+        issue_ring(sm, idx_row, t0 / 8, top_k, lane);
+        issue_ring(sm, idx_row, t0 / 8 + 1, top_k, lane);
+        wait_vmcnt<0>();
+      }
+      lds_barrier();  // Z2
+      pass(false);
     }
     // ---- epilogue: O / l.
     __syncthreads();  // E1: denominators published
@@ -618,9 +673,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   };
 
   if (wave < 4) {
-    if (hilo) score_role(std::true_type{});
-    else score_role(std::false_type{});
+    // Q fragments (B operand of the score waves): head 32 g + 16 hb + l16,
+    // k-step u covers dims 32u + 8 q4 .. +7. Loaded before the census so
+    // that the two latencies overlap.
+    bf16x8 qf[2][18];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const uint16_t* qsrc = q + ((int64_t)i * kH + 32 * (wave & 1) + 16 * hb + l16) * kDQK + 8 * q4;
+#pragma unroll
+      for (int u = 0; u < 18; ++u) qf[hb][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 32 * u));
+    }
+    census();
+    if (hilo) score_role(std::true_type{}, qf);
+    else score_role(std::false_type{}, qf);
   } else {
+    census();
     if (hilo) pv_role(std::true_type{});
     else pv_role(std::false_type{});
   }

@@ -244,6 +244,32 @@ def test_attention_arbitrary_slots(torch_cuda):
     check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "slots")
 
 
+def test_attention_long_rows_and_late_first_tile(torch_cuda):
+    # Rows longer than the 2,048 of the workloads (the index ring is refilled
+    # many times), a partial last tile (top_k = 4100), a first valid slot
+    # beyond tile 8 and one only in the last slot, and a bf16 row length that
+    # is not a multiple of 4 (plain kernel).
+    torch = torch_cuda
+    for top_k in (4100, 99):
+        cfg = synth.CONFIGS["C2"].replace(name=f"long{top_k}", n_q=6, offset=20000, top_k=top_k, seed=35)
+        inputs = synth.generate(cfg)
+        rng = np.random.default_rng(6)
+        idx = rng.integers(0, cfg.offset, size=(cfg.n_q, cfg.top_k)).astype(np.int32)
+        idx[1, :300] = -1                      # first valid tile 9
+        idx[2, :-1] = -1                       # only the last slot
+        idx[3, rng.random(cfg.top_k) < 0.9] = -1
+        idx[4, : cfg.top_k // 2] = cfg.offset + 4 + 7  # beyond query 4's position
+        dev = binding.to_device(inputs)
+        out = torch.empty((cfg.n_q, cfg.n_heads, cfg.d_latent), dtype=torch.float32, device="cuda")
+        lse = torch.empty((cfg.n_q, cfg.n_heads), dtype=torch.float32, device="cuda")
+        _say(f"long rows: top_k={top_k}")
+        binding.sparse_mla_fwd(binding.make_dims(cfg), dev["q"], dev["kv"], torch.from_numpy(idx).cuda(), out, lse)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, inputs["q"],
+                                         inputs["kv"], idx)
+        check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"long{top_k}")
+
+
 def test_chunk_invariance_and_determinism(torch_cuda):
     # The 8k chunk of C3 as four 2k chunks (offsets 8192, 10240, 12288, 14336)
     # gives the same scores and index sets; repeating a call is bitwise stable.
