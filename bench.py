@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--config", default="C3", help="workload id C0..C4 (default: 8k chunk at offset 8k)")
     ap.add_argument("--cold", action="store_true", help="overwrite a 1 GiB buffer before each step (MALL/L2 flush)")
     ap.add_argument("--cpu-baseline-s", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (reference kernel for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -130,20 +132,38 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    if args.copy_calibration:
+        # A plain device copy of known size: its rocprofv3 FETCH_SIZE / WRITE_SIZE
+        # give the scale factor between counter readings and bytes moved.
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    wall = 0.0
-    for s in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(s))
+    if flush is None:
+        # warm: the K steps run back to back inside one synchronised bracket
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        step(events[s])
+        for s in range(args.steps):
+            step(events[s])
         torch.cuda.synchronize()
-        wall += time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+    else:
+        # cold: a 1 GiB write evicts L2 and MALL before each step, outside the timed brackets
+        wall = 0.0
+        for s in range(args.steps):
+            flush.fill_(float(s))
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step(events[s])
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
     k_ms = {"indexer": [], "topk": [], "attention": []}
     for ev in events:
         k_ms["indexer"].append(ev[0].elapsed_time(ev[1]))
@@ -160,6 +180,8 @@ def main():
                 "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "mla_mfma_kernel", "flops_per_launch": w_attn["flops"],
                 "avg_launch_ms": round(avg["attention"], 4)}
+    med = {k: sorted(v)[len(v) // 2] for k, v in k_ms.items()}
+    mn = {k: min(v) for k, v in k_ms.items()}
     kernels = {
         "indexer": {"ms": round(avg["indexer"], 4), "bound": "hbm",
                     "hbm_frac": round(w_idx["bytes"] / (avg["indexer"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -169,6 +191,9 @@ def main():
         "attention": {"ms": round(avg["attention"], 4), "bound": "mfma", "mfma_frac": roofline["frac"],
                       "gather_GBs": round(w_attn["gathered_bytes"] / t_attn / 1e9, 1)},
     }
+    for k in kernels:
+        kernels[k]["median_ms"] = round(med[k], 4)
+        kernels[k]["min_ms"] = round(mn[k], 4)
     cpu = None
     if args.cpu_baseline_s > 0:
         cpu = cpu_baseline(cfg, inputs, args.cpu_baseline_s)
