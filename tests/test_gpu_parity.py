@@ -218,6 +218,31 @@ def test_topk_random_floats_and_negative_zero(torch_cuda):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("off,k,ld_pad", [(7000, 2048, 0), (30000, 2048, 4), (60000, 1500, 0), (70000, 2048, 0),
+                                          (5000, 999, 1)])
+def test_topk_row_lengths(torch_cuda, off, k, ld_pad):
+    # Row lengths across every register-resident variant of the select (up to
+    # 65,536 keys per row), the global-memory variant beyond, and an unaligned
+    # leading dimension; integer-valued scores with many ties plus random
+    # floats, vs the oracle.
+    torch = torch_cuda
+    rng = np.random.default_rng(off + k)
+    n_q = 16
+    ld = off + n_q + ld_pad
+    s = rng.integers(0, 300, size=(n_q, ld)).astype(np.float32)
+    s[::2] = rng.standard_normal((n_q // 2, ld)).astype(np.float32)
+    for i in range(n_q):
+        s[i, off + i + 1:] = -np.inf
+    _say(f"topk rows: offset={off} k={k} ld={ld}")
+    st = torch.from_numpy(s).cuda()
+    idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
+    binding.topk_select(binding.make_dims(cfg), st, ld, idx)
+    torch.cuda.synchronize()
+    ref = oracle.topk_select(n_q, off, k, s)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 def test_attention_arbitrary_slots(torch_cuda):
     # -1 padding anywhere, out-of-causal-range indices, a query with no valid
     # slot (out = 0, lse = -inf), unsorted and repeated keys.
