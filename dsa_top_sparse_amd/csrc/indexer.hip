@@ -163,13 +163,143 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
   }
 }
 
+
+// d_idx = 128: the keys of a stage (64 rows x 256 B) are read from global
+// memory once per workgroup and shared by its 4 waves through LDS (double
+// buffered; the next stage's loads are in flight during this stage's MFMAs),
+// instead of every wave reading them from L2. A key row's 16-byte piece s is
+// stored at position s ^ (row & 15), so the B-operand reads (16 consecutive
+// key rows, one piece each) hit all 64 banks.
+constexpr int kIdxStageKeys = 64;
+constexpr int kIdxRowBytes = 256;  // 128 bf16
+
+__global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
+    int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
+    int n_units, int units_per_xcd, int keys_per_unit) {
+  constexpr int D = 128, KS = D / 16;
+  const int bid = blockIdx.x;
+  const int u = (bid & 7) * units_per_xcd + (bid >> 3);
+  if (u >= n_units) return;
+  const int kr = u / n_qb;
+  const int qb = u - kr * n_qb;
+  const int q0 = qb * kIdxQueries;
+  const int nrows = min(kIdxQueries, n_q - q0);
+  const int64_t k_begin = (int64_t)kr * keys_per_unit;
+  const int64_t k_end = min<int64_t>(ld, k_begin + keys_per_unit);
+  const int64_t t_ctx = (int64_t)offset + n_q;
+  const int64_t p_max = (int64_t)offset + q0 + nrows - 1;
+  if (k_begin > p_max) {  // every key of the range lies beyond every query of the block
+    fill_neg_inf(scores, ld, q0, nrows, k_begin, k_end);
+    return;
+  }
+  // keys [k_begin, k_comp) need the product; [k_comp, k_end) are past every query
+  const int64_t k_comp = min<int64_t>(k_end, p_max + 1);
+  const int n_stages = (int)((k_comp - k_begin + kIdxStageKeys - 1) / kIdxStageKeys);
+
+  __shared__ float sw[kIdxQueries][kIdxHeads];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kIdxStageKeys * kIdxRowBytes];
+  for (int e = threadIdx.x; e < kIdxQueries * kIdxHeads; e += kIdxThreads) {
+    const int q = e >> 2;
+    sw[q][e & 3] = (q < nrows) ? w[(int64_t)(q0 + q) * kIdxHeads + (e & 3)] : 0.0f;
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // Stage loads: thread t copies pieces 4 (t % 4) .. +3 of key row t / 4.
+  const int ld_row = tid >> 2, ld_p0 = 4 * (tid & 3);
+  auto load_stage = [&](int st, u32x4 (&v)[4]) {
+    const int64_t key = k_begin + (int64_t)st * kIdxStageKeys + ld_row;
+    const int64_t krow = key < t_ctx ? key : t_ctx - 1;  // clamped rows are masked later
+    const u32x4* src = reinterpret_cast<const u32x4*>(k_idx + krow * D) + ld_p0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) v[x] = src[x];
+  };
+  auto store_stage = [&](int buf, const u32x4 (&v)[4]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      *reinterpret_cast<u32x4*>(&kbuf[buf][ld_row * kIdxRowBytes + 16 * ((ld_p0 + x) ^ (ld_row & 15))]) = v[x];
+  };
+
+  // A operand: rows (query, head) = 4*q + h of this wave's 16 queries, two
+  // 32-row blocks. Lane holds row l32, k-slice 8*hi .. 8*hi+7 of each k-step.
+  bf16x8 a[2][KS];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int qrow = wave * 16 + mb * 8 + (l32 >> 2);
+    const bool ok = qrow < nrows;
+    const uint16_t* src = q_idx + ((int64_t)(q0 + (ok ? qrow : 0)) * kIdxHeads + (l32 & 3)) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = ok ? *reinterpret_cast<const u32x4*>(src + 16 * ks) : u32x4{0, 0, 0, 0};
+      a[mb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  u32x4 pre[4];
+  load_stage(0, pre);
+  store_stage(0, pre);
+  __syncthreads();
+
+  for (int st = 0; st < n_stages; ++st) {
+    const bool more = st + 1 < n_stages;
+    if (more) load_stage(st + 1, pre);  // in flight during this stage
+    const uint8_t* kb = kbuf[st & 1];
+#pragma unroll
+    for (int sub = 0; sub < kIdxStageKeys / 32; ++sub) {
+      const int64_t nb = k_begin + (int64_t)st * kIdxStageKeys + 32 * sub;
+      if (nb >= k_comp) break;  // block-uniform
+      const int64_t key = nb + l32;
+      const int krow = 32 * sub + l32;
+      bf16x8 b[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                               &kb[krow * kIdxRowBytes + 16 * ((2 * ks + hi) ^ (krow & 15))]));
+      f32x16 acc[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        acc[mb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][ks], b[ks], acc[mb], 0, 0, 0);
+      }
+      // register r of lane (l32, hi): query 2 (r / 4) + hi of the 8-query group, head r % 4, key l32
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qrow = wave * 16 + mb * 8 + 2 * g + hi;
+          if (qrow < nrows && key < k_end) {
+            float sc = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) sc = fmaf(sw[qrow][h], fmaxf(acc[mb][4 * g + h], 0.0f), sc);
+            sc = (sc == 0.0f) ? 0.0f : sc;
+            const int64_t p = (int64_t)offset + q0 + qrow;
+            __builtin_nontemporal_store(key <= p ? sc : -INFINITY, scores + (int64_t)(q0 + qrow) * ld + key);
+          }
+        }
+    }
+    if (more) {
+      store_stage((st + 1) & 1, pre);  // the other buffer: its last readers finished before the previous barrier
+      __syncthreads();
+    }
+  }
+  // Keys past every query of the block: the 32-key blocks above wrote up to
+  // the first multiple of 32 at or after k_comp (masked to -inf per row).
+  const int64_t written = min<int64_t>(k_end, k_begin + 32 * ((k_comp - k_begin + 31) / 32));
+  if (written < k_end) fill_neg_inf(scores, ld, q0, nrows, written, k_end);
+}
+
 template <int D>
 hipError_t launch_mfma(const IndexerArgs& a, hipStream_t s) {
   const int n_qb = (a.n_q + kIdxQueries - 1) / kIdxQueries;
   // Aim for >= 2048 workgroups (8 per CU) with 32-key-aligned ranges.
   int64_t target_ranges = (2048 + n_qb - 1) / n_qb;
   int64_t kpu = (a.ld + target_ranges - 1) / target_ranges;
-  kpu = ((kpu + 31) / 32) * 32;
+  kpu = ((kpu + 63) / 64) * 64;
   if (kpu < 128) kpu = 128;
   if (kpu > 1024) kpu = 1024;
   const int64_t n_kr = (a.ld + kpu - 1) / kpu;
@@ -177,6 +307,12 @@ hipError_t launch_mfma(const IndexerArgs& a, hipStream_t s) {
   if (n_units > (int64_t)1 << 30) return hipErrorInvalidValue;
   const int units_per_xcd = (int)((n_units + 7) / 8);
   const int grid = units_per_xcd * 8;
+  if (D == 128 && kpu % kIdxStageKeys == 0) {
+    hipLaunchKernelGGL(indexer_lds_kernel, dim3(grid), dim3(kIdxThreads), 0, s, a.n_q, a.offset,
+                       static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx), a.scores,
+                       a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(indexer_mfma_kernel<D>, dim3(grid), dim3(kIdxThreads), 0, s, a.n_q, a.offset,
                      static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx),
                      a.scores, a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
