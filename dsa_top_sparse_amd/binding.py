@@ -22,6 +22,7 @@ EXPORTED = (
     "dsa_topk_workspace_bytes",
     "dsa_topk_select",
     "dsa_sparse_mla_fwd",
+    "dsa_prefill_chunk",
     "dsa_status_string",
     "dsa_version",
 )
@@ -73,7 +74,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk_workspace_bytes.restype = sz
         L.dsa_topk_select.argtypes = [dp, vp, i64, vp, vp, sz, vp]
         L.dsa_sparse_mla_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp]
-        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd):
+        L.dsa_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk):
             f.restype = ctypes.c_int
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
@@ -144,6 +146,16 @@ def sparse_mla_fwd(dims: Dims, q, kv, idx, out, lse=None, stream=None) -> None:
     _check("dsa_sparse_mla_fwd", lib().dsa_sparse_mla_fwd(
         ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse),
         _stream(stream)))
+
+
+def prefill_chunk(dims: Dims, q, kv_chunk, q_idx, w_idx, k_idx_chunk, kv_cache, k_idx_cache, scores, ld: int,
+                  idx, out, lse=None, workspace=None, stream=None) -> None:
+    _contig(q, kv_chunk, q_idx, w_idx, k_idx_chunk, kv_cache, k_idx_cache, scores, idx, out, lse)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_prefill_chunk", lib().dsa_prefill_chunk(
+        ctypes.byref(dims), _ptr(q), _ptr(kv_chunk), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx_chunk),
+        _ptr(kv_cache), _ptr(k_idx_cache), _ptr(scores), int(ld), _ptr(idx), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws, _stream(stream)))
 
 
 # ---------------------------------------------------------------- plumbing

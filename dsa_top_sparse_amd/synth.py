@@ -97,6 +97,14 @@ CONFIGS: Dict[str, DsaConfig] = {
 }
 
 
+# Whole prompts from empty caches (offset 0, n_q = prompt length), for the
+# chunked-prefill driver: the pages' 8,192-token prefill and their
+# ~17.5k-token prompt, with the shapes and distributions of C1.
+PROMPTS: Dict[str, DsaConfig] = {
+    "P8K": DsaConfig("P8K_prompt8192", 8192, 0, 64, 512, 64, 4, 128, 2048, seed=5),
+    "P17K": DsaConfig("P17K_prompt17536", 17536, 0, 64, 512, 64, 4, 128, 2048, seed=6),
+}
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)

@@ -151,6 +151,34 @@ DSA_API dsa_status dsa_topk_select(const dsa_dims *dims, const float *scores, in
 DSA_API dsa_status dsa_sparse_mla_fwd(const dsa_dims *dims, const void *q, const void *kv_cache,
                               const int32_t *idx, float *out, float *lse, void *stream);
 
+/*
+ * dsa_prefill_chunk -- one chunk of a chunked prefill: the cache append that
+ * precedes the hot path, then steps 1-7.
+ *
+ * A prompt is processed as successive chunks (the feedman.me page profiles
+ * 8,192 tokens in 2,048-token chunks, and a 17.5k-token prompt). For the
+ * chunk at rows [offset, offset + n_q) this call
+ *   1. copies kv_chunk   [n_q][d_latent + d_rope] act_dtype into kv_cache[offset ..],
+ *             k_idx_chunk [n_q][d_idx]           idx_dtype into k_idx_cache[offset ..]
+ *      (no copy when a chunk pointer already equals its destination);
+ *   2. runs dsa_indexer_scores, dsa_topk_select and dsa_sparse_mla_fwd on the
+ *      chunk, with the arguments and results documented above.
+ * Because every query's results depend only on its own row of inputs and on
+ * the cache rows it can see, the outputs of a query are bit-identical however
+ * the prompt is split into chunks.
+ *
+ * Arguments as for the three calls, plus
+ *   kv_chunk, k_idx_chunk  the chunk's new cache rows (device, 16-byte aligned;
+ *                          must not partially overlap their destination)
+ *   kv_cache, k_idx_cache  caches with room for offset + n_q rows
+ * Every argument of the three steps is validated before anything is enqueued.
+ */
+DSA_API dsa_status dsa_prefill_chunk(const dsa_dims *dims, const void *q, const void *kv_chunk,
+                                     const void *q_idx, const float *w_idx, const void *k_idx_chunk,
+                                     void *kv_cache, void *k_idx_cache, float *scores, int64_t ld,
+                                     int32_t *idx, float *out, float *lse, void *workspace,
+                                     size_t ws_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 DSA_API const char *dsa_status_string(dsa_status status);
 

@@ -113,3 +113,30 @@ def test_attention_rejects_bad_arguments(L):
     assert call(dims(n_heads=8, d_latent=4000, d_rope=64)) == UNSUP
     assert call(dims(n_heads=8, top_k=5000)) == UNSUP
     assert call(dims(n_q=0), q=None, kv=None, idx=None, out=None) == OK
+
+
+def test_prefill_chunk_rejects_bad_arguments(L):
+    def call(d, ld=None, **kw):
+        a = dict(q=FAKE, kv_chunk=FAKE, q_idx=FAKE, w=FAKE, kx_chunk=FAKE, kv_cache=FAKE * 2,
+                 kx_cache=FAKE * 4, scores=FAKE, idx=FAKE, out=FAKE, lse=None)
+        a.update(kw)
+        ld = d.offset + d.n_q if ld is None else ld
+        return L.dsa_prefill_chunk(ctypes.byref(d), a["q"], a["kv_chunk"], a["q_idx"], a["w"], a["kx_chunk"],
+                                   a["kv_cache"], a["kx_cache"], a["scores"], ld, a["idx"], a["out"], a["lse"],
+                                   None, 0, None)
+
+    assert L.dsa_prefill_chunk(None, *([FAKE] * 8), 200, FAKE, FAKE, None, None, 0, None) == NULL
+    # each step's checks run before anything is enqueued
+    assert call(dims(idx_dtype=9)) == DTYPE
+    assert call(dims(), ld=100) == SHAPE
+    assert call(dims(top_k=0)) == SHAPE
+    assert call(dims(sm_scale=float("nan"))) == SHAPE
+    assert call(dims(), kv_chunk=None) == NULL
+    assert call(dims(), kx_chunk=FAKE + 4) == ALIGN
+    assert call(dims(), scores=None) == NULL
+    # a chunk that partially overlaps its destination rows
+    d = dims()
+    dst = FAKE * 2 + d.offset * 1152
+    assert call(d, kv_chunk=dst + 1152) == SHAPE
+    assert call(dims(n_q=0), q=None, kv_chunk=None, q_idx=None, w=None, kx_chunk=None, kv_cache=None,
+                kx_cache=None, scores=None, idx=None, out=None) == OK

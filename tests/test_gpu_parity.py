@@ -297,7 +297,8 @@ def test_attention_long_rows_and_late_first_tile(torch_cuda):
 
 def test_chunk_invariance_and_determinism(torch_cuda):
     # The 8k chunk of C3 as four 2k chunks (offsets 8192, 10240, 12288, 14336)
-    # gives the same scores and index sets; repeating a call is bitwise stable.
+    # gives the same scores, index sets, outputs and lse, bit for bit;
+    # repeating a call is bitwise stable.
     torch = torch_cuda
     cfg = synth.CONFIGS["C3"]
     inputs = synth.generate(cfg)
@@ -305,6 +306,7 @@ def test_chunk_invariance_and_determinism(torch_cuda):
     dev, outs = run_gpu(torch, cfg, inputs)
     whole_idx = outs["idx"].clone()
     whole_out = outs["out"].clone()
+    whole_lse = outs["lse"].clone()
     binding.run_chunk(cfg, dev, outs)
     torch.cuda.synchronize()
     assert torch.equal(outs["idx"], whole_idx) and torch.equal(outs["out"], whole_out)
@@ -320,6 +322,40 @@ def test_chunk_invariance_and_determinism(torch_cuda):
         torch.cuda.synchronize()
         assert torch.equal(souts["idx"], whole_idx[rows])
         assert torch.equal(souts["scores"], outs["scores"][rows, : sub.t_ctx])
+        # attention outputs are chunk-invariant too (each query's work depends only on its own row)
+        assert torch.equal(souts["out"], whole_out[rows])
+        assert torch.equal(souts["lse"], whole_lse[rows])
+
+
+def test_chunked_prefill_replay(torch_cuda):
+    # The pages' 8,192-token prefill from empty caches, in 2,048-token chunks
+    # (offsets 0 / 2,048 / 4,096 / 6,144) through dsa_prefill_chunk, against
+    # the same prompt as one 8,192-token chunk: caches, index sets, outputs
+    # and lse are bit-identical; sampled rows (around chunk edges) match the
+    # oracle.
+    from dsa_top_sparse_amd import prefill
+    torch = torch_cuda
+    cfg = synth.PROMPTS["P8K"]
+    inputs = synth.generate(cfg)
+    dev = binding.to_device(inputs)
+    runs = {}
+    for chunk in (8192, 2048, 1000):
+        _say(f"prefill replay: chunk {chunk}")
+        o = prefill.alloc_prompt_outputs(cfg)
+        prefill.run_prefill(cfg, dev, chunk, o)
+        torch.cuda.synchronize()
+        runs[chunk] = o
+    whole = runs[8192]
+    assert torch.equal(whole["kv_cache"].view(torch.int16), dev["kv"].view(torch.int16))
+    assert torch.equal(whole["kidx_cache"].view(torch.int16), dev["kidx"].view(torch.int16))
+    for chunk in (2048, 1000):
+        for key in ("idx", "out", "lse"):
+            assert torch.equal(runs[chunk][key], whole[key]), (chunk, key)
+    rows = [0, 1, 999, 1000, 2047, 2048, 2049, 4095, 4096, 6143, 6144, 8191]
+    ref = oracle.full_path(cfg, inputs, rows=rows)
+    assert np.array_equal(whole["idx"][rows].cpu().numpy(), ref["idx"])
+    check_attention(whole["out"][rows].cpu().numpy(), whole["lse"][rows].cpu().numpy(), ref["out"], ref["lse"],
+                    "prefill replay")
 
 
 def test_attention_reference_restart(torch_cuda):
