@@ -116,6 +116,48 @@ def prefill_replay(torch, cfg, dev, stream, reps: int = 5):
     return res
 
 
+def decode_steps(torch, cfg, dev, stream, reps: int = 20):
+    """Decode-shaped DSA: 1 and 4 new tokens attending to the bench workload's
+    whole cache (indexer -> top-k -> split attention), HIP-event latency of the
+    step and of the attention call alone (split vs. one workgroup per query)."""
+    from dsa_top_sparse_amd import binding
+    T = cfg.t_ctx
+    res = {"workload": f"decode against a {T}-token cache"}
+    for n in (1, 4):
+        dcfg = cfg.replace(n_q=n, offset=T - n)
+        dims = binding.make_dims(dcfg)
+        q, qidx, w = dev["q"][-n:], dev["qidx"][-n:], dev["w"][-n:]
+        scores = torch.empty((n, T), dtype=torch.float32, device="cuda")
+        idx = torch.empty((n, dcfg.top_k), dtype=torch.int32, device="cuda")
+        out = torch.empty((n, dcfg.n_heads, dcfg.d_latent), dtype=torch.float32, device="cuda")
+        lse = torch.empty((n, dcfg.n_heads), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, binding.sparse_mla_decode_workspace_bytes(dims)), dtype=torch.uint8, device="cuda")
+
+        def step():
+            binding.indexer_scores(dims, qidx, w, dev["kidx"], scores, T, stream)
+            binding.topk_select(dims, scores, T, idx, None, stream)
+            binding.sparse_mla_decode(dims, q, dev["kv"], idx, out, lse, ws, stream)
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return round(1e3 * e0.elapsed_time(e1) / reps, 1)
+
+        res[f"n{n}"] = {
+            "step_us": timed(step),
+            "attention_split_us": timed(lambda: binding.sparse_mla_decode(dims, q, dev["kv"], idx, out, lse, ws,
+                                                                          stream)),
+            "attention_unsplit_us": timed(lambda: binding.sparse_mla_fwd(dims, q, dev["kv"], idx, out, lse, stream)),
+        }
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,7 +167,8 @@ def main():
     ap.add_argument("--cold", action="store_true", help="overwrite a 1 GiB buffer before each step (MALL/L2 flush)")
     ap.add_argument("--cpu-baseline-s", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-replay", dest="replay", action="store_false",
-                    help="skip the chunked-prefill replay (8,192 tokens from empty caches in 2,048-token chunks)")
+                    help="skip the side measurements: chunked-prefill replay (8,192 tokens from empty caches in "
+                         "2,048-token chunks) and decode steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference kernel for the HBM byte counters)")
     args = ap.parse_args()
@@ -225,6 +268,7 @@ def main():
         kernels[k]["median_ms"] = round(med[k], 4)
         kernels[k]["min_ms"] = round(mn[k], 4)
     replay = prefill_replay(torch, cfg, dev, stream) if args.replay else None
+    decode = decode_steps(torch, cfg, dev, stream) if args.replay else None
     cpu = None
     if args.cpu_baseline_s > 0:
         cpu = cpu_baseline(cfg, inputs, args.cpu_baseline_s)
@@ -240,6 +284,8 @@ def main():
     }
     if replay is not None:
         line["prefill_replay"] = replay
+    if decode is not None:
+        line["decode"] = decode
     print(json.dumps(line), flush=True)
 
 

@@ -23,6 +23,8 @@ EXPORTED = (
     "dsa_topk_select",
     "dsa_sparse_mla_fwd",
     "dsa_prefill_chunk",
+    "dsa_sparse_mla_decode_workspace_bytes",
+    "dsa_sparse_mla_decode",
     "dsa_status_string",
     "dsa_version",
 )
@@ -75,7 +77,11 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk_select.argtypes = [dp, vp, i64, vp, vp, sz, vp]
         L.dsa_sparse_mla_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp]
         L.dsa_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
-        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk):
+        L.dsa_sparse_mla_decode_workspace_bytes.argtypes = [dp]
+        L.dsa_sparse_mla_decode_workspace_bytes.restype = sz
+        L.dsa_sparse_mla_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk,
+                  L.dsa_sparse_mla_decode):
             f.restype = ctypes.c_int
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
@@ -145,6 +151,18 @@ def sparse_mla_fwd(dims: Dims, q, kv, idx, out, lse=None, stream=None) -> None:
     _contig(q, kv, idx, out, lse)
     _check("dsa_sparse_mla_fwd", lib().dsa_sparse_mla_fwd(
         ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
+def sparse_mla_decode_workspace_bytes(dims: Dims) -> int:
+    return int(lib().dsa_sparse_mla_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def sparse_mla_decode(dims: Dims, q, kv, idx, out, lse=None, workspace=None, stream=None) -> None:
+    _contig(q, kv, idx, out, lse, workspace)
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_sparse_mla_decode", lib().dsa_sparse_mla_decode(
+        ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse), _ptr(workspace), ws,
         _stream(stream)))
 
 

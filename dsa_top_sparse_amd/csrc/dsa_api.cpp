@@ -126,6 +126,26 @@ dsa_status dsa_sparse_mla_fwd(const dsa_dims* dims, const void* q, const void* k
   return from_hip(dsa::launch_mla(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t dsa_sparse_mla_decode_workspace_bytes(const dsa_dims* dims) {
+  if (check_chunk(dims) != DSA_OK || dims->n_q <= 0 || dims->top_k < 1 || dims->top_k > dsa::kTopkMax) return 0;
+  dsa::MlaArgs a{dims->n_q, dims->offset, dims->n_heads, dims->d_latent, dims->d_rope, dims->top_k,
+                 dims->sm_scale, dims->act_dtype == DSA_BF16, nullptr, nullptr, nullptr, nullptr, nullptr};
+  return dsa::mla_decode_workspace_bytes(a);
+}
+
+dsa_status dsa_sparse_mla_decode(const dsa_dims* dims, const void* q, const void* kv_cache, const int32_t* idx,
+                                 float* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  dsa::MlaArgs a{};
+  const dsa_status st = check_mla(dims, q, kv_cache, idx, out, lse, &a);
+  if (st != DSA_OK || dims->n_q == 0) return st;
+  const size_t need = dsa::mla_decode_workspace_bytes(a);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  }
+  return from_hip(dsa::launch_mla_decode(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_prefill_chunk(const dsa_dims* dims, const void* q, const void* kv_chunk, const void* q_idx,
                              const float* w_idx, const void* k_idx_chunk, void* kv_cache, void* k_idx_cache,
                              float* scores, int64_t ld, int32_t* idx, float* out, float* lse, void* workspace,

@@ -49,4 +49,16 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
 
+// Decode-shaped attention (few queries): each query's slots are split over
+// several workgroups whose partial results a combine kernel merges.
+struct MlaSplit {
+  int splits;       // 1 = no split (plain launch)
+  int split_slots;  // slots per split, a multiple of 32
+};
+constexpr int kDecodeTargetGroups = 256;  // workgroups to aim for
+constexpr int kDecodeMinSlots = 128;      // smallest split
+MlaSplit mla_decode_split(const MlaArgs& a);
+size_t mla_decode_workspace_bytes(const MlaArgs& a);
+hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t s);
+
 }  // namespace dsa

@@ -305,19 +305,28 @@ __device__ __forceinline__ void issue_ring(MlaSmem& sm, const int32_t* __restric
 // head's passed kRefLog2 (P could leave the range in which the fp32 sums
 // stay accurate), the query is computed once more with each head's
 // reference raised to its maximum.
-__global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offset, int top_k, float scale_log2,
-                                                               const uint16_t* __restrict__ q,
+//
+// Split launch (gridDim.y > 1): workgroup (x, y) handles slots
+// [y * split_slots, +split_slots) of the query's index row as if they were
+// the whole row, and writes its normalised output and lse to slot y of the
+// partial arrays (out / lse of shape [splits][n_q][...]); a combine kernel
+// merges the splits.
+__global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offset, int row_slots, int split_slots,
+                                                               float scale_log2, const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ kv,
                                                                const int32_t* __restrict__ idx,
                                                                float* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) MlaSmem sm;
   const int i = n_q - 1 - (int)blockIdx.x;  // latest queries (most keys) first
+  const int split = blockIdx.y;
+  const int top_k = min(split_slots, row_slots - split * split_slots);  // slots of this workgroup
+  const int64_t out_row = (int64_t)split * n_q + i;
   const uint32_t p32 = (uint32_t)(offset + i);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int32_t* __restrict__ idx_row = idx + (int64_t)i * top_k;
+  const int32_t* __restrict__ idx_row = idx + (int64_t)i * row_slots + (int64_t)split * split_slots;
   const uint8_t* __restrict__ kvb = reinterpret_cast<const uint8_t*>(kv);
   const uint32_t stage0_lds = lds_addr(sm.stage[0]);
   const uint32_t pbuf_lds = lds_addr(sm.pbuf[0]);
@@ -558,7 +567,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const float l_run = sm.lsum[0][head[hb]] + sm.lsum[1][head[hb]];
-        lse[(int64_t)i * kH + head[hb]] =
+        lse[out_row * kH + head[hb]] =
             (l_run > 0.0f) ? (m_ref[hb] + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f : -INFINITY;
       }
     }
@@ -654,7 +663,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     }
     // ---- epilogue: O / l.
     __syncthreads();  // E1: denominators published
-    float* __restrict__ orow = out + (int64_t)i * kH * kDL + 128 * v + l16;
+    float* __restrict__ orow = out + out_row * kH * kDL + 128 * v + l16;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       float f[4];
@@ -693,7 +702,77 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   }
 }
 
+// Merge of the split partials: for each (query, head), with per-split lse_s
+// and normalised outputs o_s, lse = log sum_s exp(lse_s) and
+// out = sum_s exp(lse_s - lse) o_s (splits without a valid slot have
+// lse_s = -inf and weight 0). One workgroup per (query, head), 4 dims per thread.
+constexpr int kCombineThreads = kDL / 4;
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(int n_q, int splits,
+                                                                      const float* __restrict__ part_out,
+                                                                      const float* __restrict__ part_lse,
+                                                                      float* __restrict__ out, float* __restrict__ lse) {
+  const int i = blockIdx.x, h = blockIdx.y;
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, part_lse[((int64_t)s * n_q + i) * kH + h]);
+  f32x4 acc = {0, 0, 0, 0};
+  float sum = 0.0f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float ls = part_lse[((int64_t)s * n_q + i) * kH + h];
+      const float wgt = expf(ls - m);  // 0 for an empty split
+      sum += wgt;
+      if (wgt != 0.0f) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(part_out + (((int64_t)s * n_q + i) * kH + h) * kDL +
+                                                        4 * threadIdx.x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+      }
+    }
+  }
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] *= inv;
+  *reinterpret_cast<f32x4*>(out + ((int64_t)i * kH + h) * kDL + 4 * threadIdx.x) = acc;
+  if (lse && threadIdx.x == 0) lse[(int64_t)i * kH + h] = sum > 0.0f ? m + logf(sum) : -INFINITY;
+}
+
 }  // namespace
+
+MlaSplit mla_decode_split(const MlaArgs& a) {
+  MlaSplit sp{1, a.top_k};
+  if (!mla_fast_path(a) || a.n_q <= 0) return sp;
+  // enough workgroups to occupy the chip (one per CU), splits of whole tiles
+  const int want = (kDecodeTargetGroups + a.n_q - 1) / a.n_q;
+  const int max_splits = (a.top_k + kDecodeMinSlots - 1) / kDecodeMinSlots;
+  const int splits = want < max_splits ? want : max_splits;
+  if (splits <= 1) return sp;
+  int slots = (a.top_k + splits - 1) / splits;
+  slots = (slots + kTile - 1) / kTile * kTile;
+  sp.splits = (a.top_k + slots - 1) / slots;
+  sp.split_slots = slots;
+  return sp;
+}
+
+size_t mla_decode_workspace_bytes(const MlaArgs& a) {
+  const MlaSplit sp = mla_decode_split(a);
+  if (sp.splits <= 1) return 0;
+  return (size_t)sp.splits * a.n_q * kH * (kDL + 1) * sizeof(float);
+}
+
+hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  const MlaSplit sp = mla_decode_split(a);
+  if (sp.splits <= 1) return launch_mla(a, s);
+  float* part_out = static_cast<float*>(workspace);
+  float* part_lse = part_out + (size_t)sp.splits * a.n_q * kH * kDL;
+  const float scale_log2 = a.sm_scale * 1.44269504088896340736f;
+  hipLaunchKernelGGL(mla_mfma_kernel, dim3(a.n_q, sp.splits), dim3(kThreads), 0, s, a.n_q, a.offset, a.top_k,
+                     sp.split_slots, scale_log2, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.kv), a.idx, part_out, part_lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.n_q, kH), dim3(kCombineThreads), 0, s, a.n_q, sp.splits, part_out,
+                     part_lse, a.out, a.lse);
+  return hipGetLastError();
+}
 
 bool mla_fast_path(const MlaArgs& a) {
   // top_k % 4 == 0: the index ring is filled with 16-byte loads from 16-byte aligned rows.
@@ -706,8 +785,9 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   if (mla_fast_path(a)) {
     const float scale_log2 = a.sm_scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL(mla_mfma_kernel, dim3(a.n_q), dim3(kThreads), 0, s, a.n_q, a.offset, a.top_k, scale_log2,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv), a.idx, a.out, a.lse);
+    hipLaunchKernelGGL(mla_mfma_kernel, dim3(a.n_q, 1), dim3(kThreads), 0, s, a.n_q, a.offset, a.top_k, a.top_k,
+                       scale_log2, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv), a.idx,
+                       a.out, a.lse);
     return hipGetLastError();
   }
   const int d_qk = a.d_latent + a.d_rope;

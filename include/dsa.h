@@ -152,6 +152,26 @@ DSA_API dsa_status dsa_sparse_mla_fwd(const dsa_dims *dims, const void *q, const
                               const int32_t *idx, float *out, float *lse, void *stream);
 
 /*
+ * Decode-shaped attention: steps 3-7 for a chunk of a few queries (1-4 tokens
+ * of a decode step, e.g. multi-token drafts), the decode side of the
+ * feedman.me page's split (decode runs on the machine holding the cache).
+ *
+ * Same operation, arguments and results as dsa_sparse_mla_fwd (within fp32
+ * rounding: the order of the softmax sums differs). On the fast path each
+ * query's index row is split into slices of whole 32-slot tiles that run on
+ * separate workgroups; their normalised partial outputs and log-sum-exps are
+ * merged by a second kernel. The partials live in the caller's workspace:
+ *   workspace  device buffer of ws_bytes >= dsa_sparse_mla_decode_workspace_bytes(dims),
+ *              16-byte aligned (may be NULL when that size is 0: no split)
+ * dsa_sparse_mla_decode_workspace_bytes returns 0 for dims that need no split
+ * (many queries, or the plain kernel) and for invalid dims.
+ */
+DSA_API size_t dsa_sparse_mla_decode_workspace_bytes(const dsa_dims *dims);
+DSA_API dsa_status dsa_sparse_mla_decode(const dsa_dims *dims, const void *q, const void *kv_cache,
+                                         const int32_t *idx, float *out, float *lse, void *workspace,
+                                         size_t ws_bytes, void *stream);
+
+/*
  * dsa_prefill_chunk -- one chunk of a chunked prefill: the cache append that
  * precedes the hot path, then steps 1-7.
  *

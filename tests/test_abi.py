@@ -140,3 +140,26 @@ def test_prefill_chunk_rejects_bad_arguments(L):
     assert call(d, kv_chunk=dst + 1152) == SHAPE
     assert call(dims(n_q=0), q=None, kv_chunk=None, q_idx=None, w=None, kx_chunk=None, kv_cache=None,
                 kx_cache=None, scores=None, idx=None, out=None) == OK
+
+
+def test_decode_workspace_and_bad_arguments(L):
+    d = dims(n_q=4, offset=40000)
+    ws = L.dsa_sparse_mla_decode_workspace_bytes(ctypes.byref(d))
+    # 4 queries x 16 splits of 128 slots x 64 heads x (512 + 1) fp32
+    assert ws == 16 * 4 * 64 * 513 * 4
+    assert L.dsa_sparse_mla_decode_workspace_bytes(ctypes.byref(dims(n_q=8192))) == 0  # enough queries: no split
+    assert L.dsa_sparse_mla_decode_workspace_bytes(ctypes.byref(dims(n_q=4, act_dtype=1))) == 0  # plain kernel
+    assert L.dsa_sparse_mla_decode_workspace_bytes(ctypes.byref(dims(n_q=-1))) == 0
+
+    def call(dd, ws_ptr=FAKE, ws_bytes=ws, **kw):
+        a = dict(q=FAKE, kv=FAKE, idx=FAKE, out=FAKE, lse=None)
+        a.update(kw)
+        return L.dsa_sparse_mla_decode(ctypes.byref(dd), a["q"], a["kv"], a["idx"], a["out"], a["lse"], ws_ptr,
+                                       ws_bytes, None)
+
+    assert call(d, ws_ptr=None) == WS
+    assert call(d, ws_bytes=ws - 1) == WS
+    assert call(d, ws_ptr=FAKE + 4) == ALIGN
+    assert call(dims(n_q=4, top_k=0)) == SHAPE
+    assert call(d, out=None) == NULL
+    assert call(dims(n_q=0), q=None, kv=None, idx=None, out=None, ws_ptr=None, ws_bytes=0) == OK

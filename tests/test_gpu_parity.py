@@ -358,6 +358,58 @@ def test_chunked_prefill_replay(torch_cuda):
                     "prefill replay")
 
 
+@pytest.mark.parametrize("n_q", [1, 3, 4, 40])
+def test_decode_step(torch_cuda, n_q):
+    # A decode step (1-4 tokens, and a 40-token draft) against a ~49k-token
+    # cache: indexer -> top-k -> split attention, vs the oracle and vs the
+    # unsplit attention call.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C4"].replace(name=f"decode{n_q}", n_q=n_q, offset=49152 - n_q, seed=40 + n_q,
+                                      dup_frac=0.0)
+    inputs = synth.generate(cfg)
+    dev, outs = run_gpu(torch, cfg, inputs)  # indexer + top-k + unsplit attention
+    dims = binding.make_dims(cfg)
+    ws_bytes = binding.sparse_mla_decode_workspace_bytes(dims)
+    assert ws_bytes > 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(outs["out"])
+    lse = torch.empty_like(outs["lse"])
+    _say(f"decode: n_q={n_q} ws={ws_bytes}")
+    binding.sparse_mla_decode(dims, dev["q"], dev["kv"], outs["idx"], out, lse, ws)
+    torch.cuda.synchronize()
+    ref = oracle.full_path(cfg, inputs)
+    assert np.array_equal(outs["idx"].cpu().numpy(), ref["idx"])
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref["out"], ref["lse"], f"decode{n_q}")
+    # splits of <= 128 slots take the hi/lo-P path, so the split result is the
+    # more accurate one; the two agree to the parity tolerance
+    assert float((out - outs["out"]).abs().max()) <= ATOL
+    assert float((lse - outs["lse"]).abs().max()) <= LSE_ATOL
+
+
+def test_decode_empty_and_partial_splits(torch_cuda):
+    # Index rows whose first half (eight whole splits) holds no valid slot, a
+    # row with a single valid slot, and a row with none.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C4"].replace(name="decode_pad", n_q=3, offset=20000, seed=47, dup_frac=0.0)
+    inputs = synth.generate(cfg)
+    rng = np.random.default_rng(8)
+    idx = rng.integers(0, cfg.offset, size=(cfg.n_q, cfg.top_k)).astype(np.int32)
+    idx[0, :1024] = -1
+    idx[1, :] = -1
+    idx[1, 1500] = 777
+    idx[2, :] = -1
+    dev = binding.to_device(inputs)
+    dims = binding.make_dims(cfg)
+    ws = torch.empty(binding.sparse_mla_decode_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.n_q, cfg.n_heads, cfg.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.n_q, cfg.n_heads), dtype=torch.float32, device="cuda")
+    binding.sparse_mla_decode(dims, dev["q"], dev["kv"], torch.from_numpy(idx).cuda(), out, lse, ws)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, inputs["q"], inputs["kv"], idx)
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "decode_pad")
+    assert np.all(out[2].cpu().numpy() == 0.0) and np.all(np.isneginf(lse[2].cpu().numpy()))
+
+
 def test_attention_reference_restart(torch_cuda):
     # One selected key, in a late tile, is aligned with head 5's query so that
     # its logit exceeds every logit of the first tile by ~60 (natural log):
