@@ -445,6 +445,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     for (int x = 0; x < 4; ++x) qk_lat[x] = lat_off(krow, 4 * x + q4);
 #pragma unroll
     for (int x = 0; x < 2; ++x) qk_rope[x] = rope_off(krow, 4 * x + q4);
+    // A logit in log2 units. The product is rounded on its own and never
+    // fused into a following subtraction, so that the maximal logit of the
+    // reference tile gives exactly 0 - and P = 1 - wherever it is computed.
+    auto scaled = [&](float acc) {
+#pragma clang fp contract(off)
+      return acc * scale_log2;
+    };
     // P write position of this lane's 4 slots 16 s + 4 q4 .. +3 in each head row.
     uint32_t poff[2];
 #pragma unroll
@@ -501,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
               float lm = -INFINITY;
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (vm[r]) lm = fmaxf(lm, sacc[hb][r] * scale_log2);
+                if (vm[r]) lm = fmaxf(lm, scaled(sacc[hb][r]));
               const float hm = max_over_q4(lm);
               if (q4 == 0) sm.hmax[s][head[hb]] = hm;
             }
@@ -516,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
           for (int hb = 0; hb < 2; ++hb) {
             float x[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = vm[r] ? sacc[hb][r] * scale_log2 - m_ref[hb] : -INFINITY;
+            for (int r = 0; r < 4; ++r) x[r] = vm[r] ? scaled(sacc[hb][r]) - m_ref[hb] : -INFINITY;
             runmax[hb] = fmaxf(runmax[hb], fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
             float pv[4];
 #pragma unroll
