@@ -32,6 +32,7 @@ CSRC = os.path.join(ROOT, "dsa_top_sparse_amd", "csrc")
 KERNELS = {
     "mla_mfma_kernel": ("sparse_mla.hip", "mla_mfma_kernel"),
     "indexer_mfma_kernel": ("indexer.hip", "indexer_mfma_kernel"),
+    "indexer_lds_kernel": ("indexer.hip", "indexer_lds_kernel"),
     "topk_kernel": ("topk.hip", "topk_kernel"),
 }
 COPY_KERNEL = "copyBuffer"
