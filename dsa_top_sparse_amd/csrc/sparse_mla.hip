@@ -459,9 +459,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 
     float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.0f, 0.0f}, runmax[2] = {-INFINITY, -INFINITY};
 
+    // Ring entries used in iteration t (the rows of tile t + kAhead, the slot
+    // indices of tile t) are read in iteration t - 1, so that no LDS read
+    // latency sits between the barrier and the first operand reads.
+    auto ring_rows = [&](int t) {
+      const int tn = t + kAhead;
+      return gather_rows(sm.ring[(tn < n_tiles ? tn : t0) % kRingTiles], tn, wave, lane, top_k, p32);
+    };
+    auto ring_slots = [&](int t) { return *reinterpret_cast<const u32x4*>(&sm.ring[t % kRingTiles][16 * s + 4 * q4]); };
     auto pass = [&](const bf16x8 (&qf)[2][18], bool first_pass) {
       start_pipeline(kAhead);
       int st = 0;  // stage of tile t
+      GatherRows rows = ring_rows(t0);
+      u32x4 jv = ring_slots(t0);
       for (int t = t0; t <= n_tiles; ++t) {
         wait_tile(t, hilo_c);
         lds_barrier();  // B(t): tile t resident; P(t - 1) complete
@@ -470,7 +480,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
         int sn = st + kAhead;
         if (sn >= S) sn -= S;
         const uint32_t next_lds = stage0_lds + kStageBytes * sn;
-        const GatherRows rows = gather_rows(sm.ring[(more ? t_next : t0) % kRingTiles], t_next, wave, lane, top_k, p32);
+        GatherRows rows_n;
+        u32x4 jv_n;
         if (t < n_tiles && t >= first_tile) {
           // ---- S^T = K Q^T; tile t + kAhead's loads go out between the MFMAs
           const uint32_t tile_lds = stage0_lds + kStageBytes * st;
@@ -496,8 +507,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
               sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[hb][u], sacc[hb], 0, 0, 0);
             if (more && u % 3 == 1 && u / 3 < 5) gather_load(kvb, rows, next_lds, lane16, rope_lane, u / 3, wave);
           }
+          rows_n = ring_rows(t + 1);
+          jv_n = ring_slots(t + 1);
           // ---- slot validity (from the ring)
-          const u32x4 jv = *reinterpret_cast<const u32x4*>(&sm.ring[t % kRingTiles][16 * s + 4 * q4]);
           const int gs0 = t * kTile + 16 * s + 4 * q4;
           bool vm[4];
 #pragma unroll
@@ -538,9 +550,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
               lds_write8(plo_lds + par + poff[hb], u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)});
             }
           }
-        } else if (more) {
-          issue_all(rows, next_lds);
+        } else {
+          if (more) issue_all(rows, next_lds);
+          rows_n = ring_rows(t + 1);
+          jv_n = ring_slots(t + 1);
         }
+        rows = rows_n;
+        jv = jv_n;
         st = (st + 1 == S) ? 0 : st + 1;
       }
     };
@@ -603,9 +619,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) o[mb][nb] = f32x4{0, 0, 0, 0};
 
+    auto ring_rows = [&](int t) {  // read one iteration ahead, as in the score waves
+      const int tn = t + kAhead;
+      return gather_rows(sm.ring[(tn < n_tiles ? tn : t0) % kRingTiles], tn, wave, lane, top_k, p32);
+    };
     auto pass = [&](bool first_pass) {
       start_pipeline(kAhead);
       int st = 0;  // stage of tile t
+      GatherRows rows = ring_rows(t0);
       for (int t = t0; t <= n_tiles; ++t) {
         wait_tile(t, hilo_c);
         lds_barrier();  // B(t)
@@ -616,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
         int sn = st + kAhead;
         if (sn >= S) sn -= S;
         const uint32_t next_lds = stage0_lds + kStageBytes * sn;
-        const GatherRows rows = gather_rows(sm.ring[(more ? t_next : t0) % kRingTiles], t_next, wave, lane, top_k, p32);
+        GatherRows rows_n;
         if (t - 1 >= first_tile) {
           // ---- O += P V for tile t - 1; tile t + kAhead's loads go out between the MFMAs
           const uint32_t tile_lds = stage0_lds + kStageBytes * (st == 0 ? S - 1 : st - 1);
@@ -642,11 +663,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
               for (int mb = 0; mb < 4; ++mb)
                 o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], cur, o[mb][nb], 0, 0, 0);
               if (more && part == 0 && (nb & 1) == 0) gather_load(kvb, rows, next_lds, lane16, rope_lane, nb >> 1, wave);
+              if (part == 0 && nb == 5) rows_n = ring_rows(t + 1);
             }
           }
-        } else if (more) {
-          issue_all(rows, next_lds);
+        } else {
+          if (more) issue_all(rows, next_lds);
+          rows_n = ring_rows(t + 1);
         }
+        rows = rows_n;
         // X: the score waves' reference exchange (same condition as theirs)
         if (first_pass && t == first_tile && t < n_tiles) lds_barrier();
         st = (st + 1 == S) ? 0 : st + 1;
@@ -688,18 +712,31 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     }
   };
 
+  // The query's Q block (64 heads x 576 dims, 72 KB, contiguous) is copied
+  // into stages 2-3 by all 8 waves (9 direct-to-LDS loads each) before the
+  // census, whose wait covers it; the score waves then take their fragments
+  // from LDS. The stages are not loaded before the first tile iteration.
+  {
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(q) + (int64_t)i * (kH * kRowBytes);
+    const uint32_t q_lds = stage0_lds + 2 * kStageBytes;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      const uint32_t chunk = (uint32_t)(8 * c + wave);
+      dma16(qb, 1024u * chunk + lane16, q_lds + 1024u * chunk);
+    }
+  }
   if (wave < 4) {
+    census();
     // Q fragments (B operand of the score waves): head 32 g + 16 hb + l16,
-    // k-step u covers dims 32u + 8 q4 .. +7. Loaded before the census so
-    // that the two latencies overlap.
+    // k-step u covers dims 32u + 8 q4 .. +7.
     bf16x8 qf[2][18];
+    const uint32_t q_lds = stage0_lds + 2 * kStageBytes;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const uint16_t* qsrc = q + ((int64_t)i * kH + 32 * (wave & 1) + 16 * hb + l16) * kDQK + 8 * q4;
+      const uint32_t qsrc = q_lds + (uint32_t)((32 * (wave & 1) + 16 * hb + l16) * kRowBytes + 16 * q4);
 #pragma unroll
-      for (int u = 0; u < 18; ++u) qf[hb][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qsrc + 32 * u));
+      for (int u = 0; u < 18; ++u) qf[hb][u] = __builtin_bit_cast(bf16x8, lds_read16(qsrc + 64 * u));
     }
-    census();
     if (hilo) score_role(std::true_type{}, qf);
     else score_role(std::false_type{}, qf);
   } else {

@@ -9,19 +9,22 @@
 //
 // One workgroup per query row, an exact radix select on the order-preserving
 // uint32 image of each score (12 + 10 + 10 bits):
-//   pass 1  (HBM): 4096-bin histogram of the top 12 bits in LDS
+//   pass 1       : 4096-bin histogram of the top 12 bits in LDS
 //                  -> bucket b1 holding the k-th largest key;
-//   pass 2  (L2) : if the keys with top bits >= b1 fit in LDS, compact them
-//                  (key, index) into LDS in index order (wave ballots +
-//                  a block scan), so every later pass runs out of LDS;
+//   pass 2       : if the keys with top bits >= b1 fit in LDS, compact them
+//                  (key, index) into LDS in index order (a block scan of
+//                  per-thread counts), so every later pass runs out of LDS;
 //   refine       : 1024-bin histograms of the next 10 and last 10 bits among
 //                  the keys of the boundary bucket -> exact threshold T and
 //                  r = number of keys equal to T that still fit;
 //   emit         : in index order, keep key > T, and key == T while fewer
 //                  than r ties have been kept; the output position of a kept
 //                  key is (#greater before it) + min(#ties before it, r).
-// If the candidates do not fit in LDS, the refine and emit passes re-read the
-// row from global memory instead (same arithmetic).
+// Rows of at most 16,384 keys (topk_reg_kernel) are read once, into
+// registers, and both passes run from there. Longer rows (topk_kernel) are
+// streamed twice from global memory, the next group's loads in flight while
+// the current group is counted. If the candidates do not fit in LDS, the
+// refine and emit passes re-read the row instead (same arithmetic).
 #include "common.h"
 #include "kernels.h"
 
@@ -44,6 +47,15 @@ struct TopkSmem {
   uint32_t bc[4];
 };
 
+// Barrier for LDS traffic only: unlike __syncthreads() it leaves this
+// thread's global loads in flight (the streaming passes prefetch across it).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Block-wide exclusive scan of a uint64 (callers pack independent counters in
 // bit fields that cannot overflow into each other). `buf` alternates between
 // calls so that a single barrier per scan suffices.
@@ -57,7 +69,7 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* total,
     if (lane >= o) x += (static_cast<uint64_t>(hi) << 32) | lo;
   }
   if (lane == kWave - 1) sm.scan[buf][wave] = x;
-  __syncthreads();
+  lds_sync();
   uint64_t before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < kTkWaves; ++w) {
@@ -116,79 +128,14 @@ __device__ __forceinline__ f32x4 load4(const float* __restrict__ row, int base, 
   return v;
 }
 
+// Refine and emit, after bucket b1 (holding the k-th largest key; above1 keys
+// lie in higher buckets, cnt1 in b1) is known and, when in_lds, the keys with
+// top bits >= b1 sit in LDS in index order.
 template <bool ALIGNED>
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, const float* __restrict__ scores,
-                                                          int64_t ld, int32_t* __restrict__ idx) {
-  __shared__ TopkSmem sm;
-  int buf = 0;
-  const int i = blockIdx.x;
-  const int n = offset + i + 1;  // causal keys 0 .. p (fits int32: validated on the host)
-  int32_t* __restrict__ out = idx + static_cast<int64_t>(i) * k;
-  if (n <= k) {
-    for (int t = threadIdx.x; t < k; t += kTkThreads) out[t] = t < n ? t : -1;
-    return;
-  }
-  const float* __restrict__ row = scores + static_cast<int64_t>(i) * ld;
+__device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float* __restrict__ row, int n, int k,
+                                            int32_t* __restrict__ out, uint32_t b1, uint32_t above1, uint32_t cnt1,
+                                            bool in_lds) {
   const int tid = threadIdx.x;
-
-  // ---- pass 1: histogram of the top 12 bits over the causal prefix.
-  for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
-  __syncthreads();
-  for (int base = 0; base < n; base += 4 * kSlice) {
-    f32x4 v[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) v[s] = load4<ALIGNED>(row, base + s * kSlice, n);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (base + s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[score_key(v[s][e]) >> 20], 1u);
-  }
-  __syncthreads();
-  uint32_t b1, above1, cnt1;
-  select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
-  const bool in_lds = above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
-
-  // ---- pass 2: ordered compaction of every key with top bits >= b1 into LDS.
-  if (in_lds) {
-    uint32_t cbase = 0;
-    for (int base = 0; base < n; base += 4 * kSlice) {
-      f32x4 v[4];
-      uint32_t key[4][4];
-      uint64_t packed = 0;  // 4 x 16-bit per-slice counts (each slice total <= 2048)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        v[s] = load4<ALIGNED>(row, base + s * kSlice, n);
-        uint32_t c = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          key[s][e] = score_key(v[s][e]);
-          const bool f = (base + s * kSlice + 4 * tid + e < n) && (key[s][e] >> 20) >= b1;
-          c += f;
-        }
-        packed |= static_cast<uint64_t>(c) << (16 * s);
-      }
-      uint64_t tot;
-      const uint64_t excl = block_excl_scan(packed, &tot, sm, buf);
-      uint32_t slice_base = cbase;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint32_t pos = slice_base + static_cast<uint32_t>((excl >> (16 * s)) & 0xFFFF);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = base + s * kSlice + 4 * tid + e;
-          if (j < n && (key[s][e] >> 20) >= b1 && pos < static_cast<uint32_t>(kTkCap)) {
-            sm.ckey[pos] = key[s][e];
-            sm.cidx[pos] = j;
-            ++pos;
-          }
-        }
-        slice_base += static_cast<uint32_t>((tot >> (16 * s)) & 0xFFFF);
-      }
-      cbase = slice_base;
-    }
-    __syncthreads();
-  }
   const int n_cand = static_cast<int>(above1 + cnt1);
 
   // ---- refine: exact threshold inside bucket b1 with two 10-bit digits.
@@ -290,12 +237,177 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
   }
 }
 
+template <bool ALIGNED>
+__global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, const float* __restrict__ scores,
+                                                          int64_t ld, int32_t* __restrict__ idx) {
+  __shared__ TopkSmem sm;
+  int buf = 0;
+  const int i = blockIdx.x;
+  const int n = offset + i + 1;  // causal keys 0 .. p (fits int32: validated on the host)
+  int32_t* __restrict__ out = idx + static_cast<int64_t>(i) * k;
+  if (n <= k) {
+    for (int t = threadIdx.x; t < k; t += kTkThreads) out[t] = t < n ? t : -1;
+    return;
+  }
+  const float* __restrict__ row = scores + static_cast<int64_t>(i) * ld;
+  const int tid = threadIdx.x;
+
+  // ---- pass 1: histogram of the top 12 bits over the causal prefix.
+  for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
+  __syncthreads();
+  // The loads of the next group go out before this group's atomics.
+  f32x4 v[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v[s] = load4<ALIGNED>(row, s * kSlice, n);
+  for (int base = 0; base < n; base += 4 * kSlice) {
+    f32x4 nx[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) nx[s] = load4<ALIGNED>(row, base + 4 * kSlice + s * kSlice, n);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (base + s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[score_key(v[s][e]) >> 20], 1u);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] = nx[s];
+  }
+  __syncthreads();
+  uint32_t b1, above1, cnt1;
+  select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
+  const bool in_lds = above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
+
+  // ---- pass 2: ordered compaction of every key with top bits >= b1 into LDS.
+  if (in_lds) {
+    uint32_t cbase = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] = load4<ALIGNED>(row, s * kSlice, n);
+    for (int base = 0; base < n; base += 4 * kSlice) {
+      f32x4 nx[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) nx[s] = load4<ALIGNED>(row, base + 4 * kSlice + s * kSlice, n);
+      uint32_t key[4][4];
+      uint64_t packed = 0;  // 4 x 16-bit per-slice counts (each slice total <= 2048)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          key[s][e] = score_key(v[s][e]);
+          const bool f = (base + s * kSlice + 4 * tid + e < n) && (key[s][e] >> 20) >= b1;
+          c += f;
+        }
+        packed |= static_cast<uint64_t>(c) << (16 * s);
+      }
+      uint64_t tot;
+      const uint64_t excl = block_excl_scan(packed, &tot, sm, buf);
+      uint32_t slice_base = cbase;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t pos = slice_base + static_cast<uint32_t>((excl >> (16 * s)) & 0xFFFF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = base + s * kSlice + 4 * tid + e;
+          if (j < n && (key[s][e] >> 20) >= b1 && pos < static_cast<uint32_t>(kTkCap)) {
+            sm.ckey[pos] = key[s][e];
+            sm.cidx[pos] = j;
+            ++pos;
+          }
+        }
+        slice_base += static_cast<uint32_t>((tot >> (16 * s)) & 0xFFFF);
+      }
+      cbase = slice_base;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) v[s] = nx[s];
+    }
+    __syncthreads();
+  }
+  select_tail<ALIGNED>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds);
+}
+
+// Rows of at most NV * 2048 keys: the row is read once, into registers
+// (thread t holds keys 2048 v + 4 t + e, all loads issued together), and
+// both the histogram and the ordered compaction run from those registers.
+template <int NV>
+__global__ __launch_bounds__(kTkThreads) void topk_reg_kernel(int offset, int k, const float* __restrict__ scores,
+                                                              int64_t ld, int32_t* __restrict__ idx) {
+  __shared__ TopkSmem sm;
+  int buf = 0;
+  const int i = blockIdx.x;
+  const int n = offset + i + 1;
+  int32_t* __restrict__ out = idx + static_cast<int64_t>(i) * k;
+  if (n <= k) {
+    for (int t = threadIdx.x; t < k; t += kTkThreads) out[t] = t < n ? t : -1;
+    return;
+  }
+  const float* __restrict__ row = scores + static_cast<int64_t>(i) * ld;
+  const int tid = threadIdx.x;
+  uint32_t key[NV][4];
+  {
+    f32x4 v[NV];
+#pragma unroll
+    for (int s = 0; s < NV; ++s) v[s] = load4<true>(row, s * kSlice, n);
+#pragma unroll
+    for (int s = 0; s < NV; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[s][e] = score_key(v[s][e]);  // -inf past n: key 0x007FFFFF
+  }
+  for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NV; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[key[s][e] >> 20], 1u);
+  __syncthreads();
+  uint32_t b1, above1, cnt1;
+  select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
+  const bool in_lds = above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
+  if (in_lds) {
+    uint32_t cbase = 0;
+#pragma unroll
+    for (int s0 = 0; s0 < NV; s0 += 4) {
+      uint64_t packed = 0;  // 4 x 16-bit per-slice counts (each slice total <= 2048)
+#pragma unroll
+      for (int s = s0; s < s0 + 4 && s < NV; ++s) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += (s * kSlice + 4 * tid + e < n) && (key[s][e] >> 20) >= b1;
+        packed |= static_cast<uint64_t>(c) << (16 * (s - s0));
+      }
+      uint64_t tot;
+      const uint64_t excl = block_excl_scan(packed, &tot, sm, buf);
+      uint32_t slice_base = cbase;
+#pragma unroll
+      for (int s = s0; s < s0 + 4 && s < NV; ++s) {
+        uint32_t pos = slice_base + static_cast<uint32_t>((excl >> (16 * (s - s0))) & 0xFFFF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = s * kSlice + 4 * tid + e;
+          if (j < n && (key[s][e] >> 20) >= b1) {
+            sm.ckey[pos] = key[s][e];
+            sm.cidx[pos] = j;
+            ++pos;
+          }
+        }
+        slice_base += static_cast<uint32_t>((tot >> (16 * (s - s0))) & 0xFFFF);
+      }
+      cbase = slice_base;
+    }
+    __syncthreads();
+  }
+  select_tail<true>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   const bool aligned = (a.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
-  if (aligned)
+  const int64_t n_max = (int64_t)a.offset + a.n_q;  // longest causal row
+  if (aligned && n_max <= 8 * kSlice)
+    hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores, a.ld,
+                       a.idx);
+  else if (aligned)
     hipLaunchKernelGGL(topk_kernel<true>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores,
                        a.ld, a.idx);
   else
