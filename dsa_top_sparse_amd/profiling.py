@@ -33,6 +33,7 @@ KERNELS = {
     "mla_mfma_kernel": ("sparse_mla.hip", "mla_mfma_kernel"),
     "indexer_mfma_kernel": ("indexer.hip", "indexer_mfma_kernel"),
     "indexer_lds_kernel": ("indexer.hip", "indexer_lds_kernel"),
+    "topk_reg_kernel": ("topk.hip", "topk_reg_kernel"),
     "topk_kernel": ("topk.hip", "topk_kernel"),
 }
 COPY_KERNEL = "copyBuffer"
