@@ -22,8 +22,15 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags. The indexer's MFMA accumulators are read by VALU code
+# right after every product: asking for the VGPR form of the MFMAs saves an
+# accumulator-to-VGPR copy per element.
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, obj: str, extra) -> None:
-    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

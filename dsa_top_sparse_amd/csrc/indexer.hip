@@ -266,19 +266,29 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
         for (int ks = 0; ks < KS; ++ks)
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][ks], b[ks], acc[mb], 0, 0, 0);
       }
-      // register r of lane (l32, hi): query 2 (r / 4) + hi of the 8-query group, head r % 4, key l32
+      // register r of lane (l32, hi): query 2 (r / 4) + hi of the 8-query group, head r % 4, key l32.
+      // ReLU as an integer max on the bits (one instruction: a negative float is a
+      // negative int32); adding +0 turns a -0 sum into +0;
+      // the causal mask is needed only where the block reaches the wave's
+      // first query (block-uniform test).
+      const bool all_causal = nb + 31 <= (int64_t)offset + q0 + wave * 16;
+      const bool all_in = nb + 32 <= k_end && q0 + wave * 16 + 16 <= n_q;  // every row and key of the sub-block exists
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qrow = wave * 16 + mb * 8 + 2 * g + hi;
-          if (qrow < nrows && key < k_end) {
+          if (all_in || (qrow < nrows && key < k_end)) {
             float sc = 0.0f;
 #pragma unroll
-            for (int h = 0; h < 4; ++h) sc = fmaf(sw[qrow][h], fmaxf(acc[mb][4 * g + h], 0.0f), sc);
-            sc = (sc == 0.0f) ? 0.0f : sc;
-            const int64_t p = (int64_t)offset + q0 + qrow;
-            __builtin_nontemporal_store(key <= p ? sc : -INFINITY, scores + (int64_t)(q0 + qrow) * ld + key);
+            for (int h = 0; h < 4; ++h)
+              sc = fmaf(sw[qrow][h], __int_as_float(max(__float_as_int(acc[mb][4 * g + h]), 0)), sc);
+            sc = sc + 0.0f;
+            if (!all_causal) {
+              const int64_t p = (int64_t)offset + q0 + qrow;
+              sc = key <= p ? sc : -INFINITY;
+            }
+            __builtin_nontemporal_store(sc, scores + (int64_t)(q0 + qrow) * ld + key);
           }
         }
     }
