@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
 // key rows, one piece each) hit all 64 banks.
 constexpr int kIdxStageKeys = 64;
 constexpr int kIdxRowBytes = 256;  // 128 bf16
+constexpr int kTbRow = 36;         // floats per row of a wave's score tile (32 keys + pad)
 
 __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
     int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -199,6 +200,8 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
 
   __shared__ float sw[kIdxQueries][kIdxHeads];
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kIdxStageKeys * kIdxRowBytes];
+  __shared__ __attribute__((aligned(16))) float tbuf[kIdxThreads / 64][16 * kTbRow];
+  const bool vec_ok = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   for (int e = threadIdx.x; e < kIdxQueries * kIdxHeads; e += kIdxThreads) {
     const int q = e >> 2;
     sw[q][e & 3] = (q < nrows) ? w[(int64_t)(q0 + q) * kIdxHeads + (e & 3)] : 0.0f;
@@ -273,6 +276,34 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
       // first query (block-uniform test).
       const bool all_causal = nb + 31 <= (int64_t)offset + q0 + wave * 16;
       const bool all_in = nb + 32 <= k_end && q0 + wave * 16 + 16 <= n_q;  // every row and key of the sub-block exists
+      if (vec_ok && all_in) {
+        // Through this wave's LDS tile, so that the stores are 16-byte vectors
+        // (4 keys of one query per lane) instead of one score per lane.
+        float* tb = tbuf[wave];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int qr = mb * 8 + 2 * g + hi;  // row inside the wave's 16 queries
+            float sc = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              sc = fmaf(sw[wave * 16 + qr][h], __int_as_float(max(__float_as_int(acc[mb][4 * g + h]), 0)), sc);
+            sc = sc + 0.0f;
+            if (!all_causal) {
+              const int64_t p = (int64_t)offset + q0 + wave * 16 + qr;
+              sc = key <= p ? sc : -INFINITY;
+            }
+            tb[qr * kTbRow + l32] = sc;
+          }
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int piece = 64 * x + lane, r = piece >> 3, c = piece & 7;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&tb[r * kTbRow + 4 * c]);
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(scores + (int64_t)(q0 + wave * 16 + r) * ld + nb + 4 * c));
+        }
+        continue;
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
