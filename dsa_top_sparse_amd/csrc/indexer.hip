@@ -10,8 +10,10 @@
 // cores. Rows of the A operand are (query, head) pairs laid out as 4*q + h, so
 // in the 32x32 MFMA result each lane holds the 4 head dot products of one
 // (query, key) pair and the ReLU / weight / head sum happens in registers.
-// Each lane then stores one fp32 score; 32 lanes cover 32 consecutive keys of
-// one query row (128-byte segments).
+// With d_idx = 128 (indexer_lds_kernel) the scores of a wave's 16 queries x
+// 32 keys pass through a small LDS tile and leave as 16-byte stores (4
+// consecutive keys of one query per lane); the other widths store one fp32
+// score per lane, 32 lanes covering 32 consecutive keys of one query row.
 #include "common.h"
 #include "kernels.h"
 

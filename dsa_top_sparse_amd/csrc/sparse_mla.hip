@@ -11,20 +11,22 @@
 // one query per threadgroup with scalar dot products, and the same paragraph
 // proposes using the matrix units -- which is what the fast kernel below does.)
 //
-// Fast kernel (bf16, 64 heads, 512 + 64 dims): one workgroup per query. The 64
-// heads of one query share every gathered latent row, so they form the M = 64
-// side of both products and no MFMA lane is wasted on masking. Per tile of 32
-// selected slots:
-//   gather  : each thread loads 16-byte pieces of the selected rows into
-//             registers one tile ahead; the rows go to LDS twice -- key-major
-//             for Q K^T and transposed (dim-major) for P V;
-//   Q K^T   : wave w owns heads 16w..16w+15; S^T = K Q^T on 16x16x32 bf16
-//             MFMAs with the query's Q fragments held in registers;
-//   softmax : fp32, exp2 with log2(e) folded into the scale, running max and
-//             sum per head; P goes to LDS as bf16 (split into hi + lo bf16
-//             parts when the query has few valid keys, where single bf16
-//             rounding of a large weight would show in the output);
-//   P V     : wave w owns output dims 128w..128w+127 for all 64 heads.
+// Fast kernel (bf16, 64 heads, 512 + 64 dims): one workgroup of 8 waves per
+// query. The 64 heads of one query share every gathered latent row, so they
+// form the M = 64 side of both products and no MFMA lane is wasted on
+// masking. Per tile of 32 selected slots:
+//   gather  : all waves issue direct-to-LDS 16-byte loads of the selected
+//             rows, two tiles ahead, into one of 4 key-major LDS stages;
+//   Q K^T   : score waves 0-3 each own 32 heads x 16 slots; S^T = K Q^T on
+//             16x16x32 bf16 MFMAs with the query's Q fragments in registers;
+//   softmax : fp32, exp2 with log2(e) folded into the scale, against a fixed
+//             per-head reference (no running rescale); P goes to LDS as bf16
+//             (split into hi + lo bf16 parts when the query has few valid
+//             keys, where single bf16 rounding of a large weight would show);
+//   P V     : P V waves 4-7 each own output dims 128v..128v+127 of all 64
+//             heads, reading V transposed out of the key-major stage.
+// The two roles run side by side on every SIMD, one tile apart, and meet at
+// one barrier per tile (details at the kernel).
 #include "common.h"
 #include "kernels.h"
 
