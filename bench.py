@@ -162,7 +162,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C3", help="workload id C0..C4 (default: 8k chunk at offset 8k)")
     ap.add_argument("--cold", action="store_true", help="overwrite a 1 GiB buffer before each step (MALL/L2 flush)")
     ap.add_argument("--cpu-baseline-s", type=float, default=12.0, help="seconds of oracle work (0 = skip)")

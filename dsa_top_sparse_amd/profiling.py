@@ -58,7 +58,10 @@ def kernel_key(name: str):
     return None
 
 
-def read_stats(trace_dir: str):
+def read_stats(trace_dir: str, skip: int = 0):
+    """rocprofv3's per-kernel statistics, plus the mean over the dispatches
+    after the first `skip` of each kernel (the bench's warm-up steps), taken
+    from the kernel trace of the same run."""
     rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
     out = {}
     for r in rows:
@@ -67,6 +70,15 @@ def read_stats(trace_dir: str):
             out[k[1]] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
                          "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
                          "pct": float(r["Percentage"])}
+    durs = {}
+    for r in csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))):
+        k = kernel_key(r["Kernel_Name"])
+        if k:
+            durs.setdefault(k[1], []).append(
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    for short, st in out.items():
+        d = [x[1] for x in sorted(durs.get(short, []))][skip:]
+        st["timed_avg_us"] = statistics.mean(d) if d else float("nan")
     return out
 
 
@@ -98,10 +110,11 @@ def main():
     ap.add_argument("--command", required=True, help="the bench command of the trace run")
     ap.add_argument("--pmc-command", default=None, help="the bench command of the counter runs (default: --command)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--skip", type=int, default=0, help="warm-up dispatches per kernel left out of the timed mean")
     args = ap.parse_args()
 
     pmc_cmd = args.pmc_command or args.command
-    stats = read_stats(args.trace)
+    stats = read_stats(args.trace, args.skip)
     fetch, fetch_copy = read_counter(args.fetch, "FETCH_SIZE")
     write, write_copy = read_counter(args.write, "WRITE_SIZE")
     f_fetch = COPY_BYTES / (fetch_copy * 1024.0)
@@ -120,18 +133,20 @@ def main():
              f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {pmc_cmd} --copy-calibration",
              "",
              "Counter scale (1 GiB device copy): FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (f_fetch, f_write), "",
-             "| kernel | calls | avg us | min us | max us | share | HBM read MB/launch | HBM write MB/launch | source sha |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             f"avg us: rocprofv3's mean over all dispatches; timed avg us: mean after the first {args.skip} "
+             "dispatches of each kernel (the bench's warm-up steps), the figure bench.py's HIP events measure.", "",
+             "| kernel | calls | avg us | timed avg us | min us | max us | share | HBM read MB/launch | HBM write MB/launch | source sha |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
     for short, st in sorted(stats.items(), key=lambda kv: -kv[1]["avg_us"]):
         src = next(v[0] for v in KERNELS.values() if v[1] == short)
         rd = fetch.get(short, float("nan")) * 1024.0 * f_fetch
         wr = write.get(short, float("nan")) * 1024.0 * f_write
         sha = source_sha(src)
-        lines.append(f"| {short} | {st['calls']} | {st['avg_us']:.1f} | {st['min_us']:.1f} | {st['max_us']:.1f} | "
+        lines.append(f"| {short} | {st['calls']} | {st['avg_us']:.1f} | {st['timed_avg_us']:.1f} | {st['min_us']:.1f} | {st['max_us']:.1f} | "
                      f"{st['pct']:.1f}% | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {sha} |")
         traffic.setdefault(args.workload, {})[src] = {
             "kernel": short, "bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
-            "fetch_scale": f_fetch, "write_scale": f_write, "avg_launch_us": st["avg_us"], "source_sha": sha}
+            "fetch_scale": f_fetch, "write_scale": f_write, "avg_launch_us": st["timed_avg_us"], "source_sha": sha}
     with open(os.path.join(args.out, f"kernels_{args.workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(traffic_path, "w") as f:
