@@ -135,11 +135,16 @@ def test_config_parity(torch_cuda, name):
         assert np.array_equal(scores.cpu().numpy().view(np.uint32), all_ref.view(np.uint32))
 
 
-def test_ragged_fast_path_all_rows(torch_cuda):
+@pytest.mark.parametrize("ld_pad", [3, 0])
+def test_ragged_fast_path_all_rows(torch_cuda, ld_pad):
     torch = torch_cuda
     cfg = synth.CONFIGS["C2"].replace(name="ragged", n_q=77, offset=1003, top_k=100, seed=31)
     inputs = synth.generate(cfg)
-    ld = cfg.t_ctx + 3  # odd row stride: the select's unaligned path, -inf padding columns
+    # ld_pad 3: odd row stride (the select's unaligned path, one score per store
+    # in the indexer, -inf padding columns); 0: t_ctx = 1,080 is a multiple of
+    # 4, so full 32-key blocks take the indexer's 16-byte stores and the
+    # partial last query block the per-score stores
+    ld = cfg.t_ctx + ld_pad
     _say(f"ragged: {cfg} ld={ld}")
     dev, outs = run_gpu(torch, cfg, inputs, ld=ld)
     ref = oracle.full_path(cfg, inputs)
