@@ -10,7 +10,7 @@
 // cores. Rows of the A operand are (query, head) pairs laid out as 4*q + h, so
 // in the 32x32 MFMA result each lane holds the 4 head dot products of one
 // (query, key) pair and the ReLU / weight / head sum happens in registers.
-// With d_idx = 128 (indexer_lds_kernel) the scores of a wave's 16 queries x
+// With d_idx = 128 (indexer_lds_kernel) the scores of a wave's 8 queries x
 // 32 keys pass through a small LDS tile and leave as 16-byte stores (4
 // consecutive keys of one query per lane); the other widths store one fp32
 // score per lane, 32 lanes covering 32 consecutive keys of one query row.
@@ -62,7 +62,7 @@ __device__ __forceinline__ void fill_neg_inf(float* __restrict__ scores, int64_t
   const int width = (int)(k1 - k0);
   for (int r = 0; r < nrows; ++r) {
     float* row = scores + (int64_t)(q0 + r) * ld + k0;
-    for (int c = threadIdx.x; c < width; c += kIdxThreads) __builtin_nontemporal_store(-INFINITY, row + c);
+    for (int c = threadIdx.x; c < width; c += (int)blockDim.x) __builtin_nontemporal_store(-INFINITY, row + c);
   }
 }
 
@@ -166,17 +166,19 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
 }
 
 
-// d_idx = 128: the keys of a stage (64 rows x 256 B) are read from global
-// memory once per workgroup and shared by its 4 waves through LDS (double
-// buffered; the next stage's loads are in flight during this stage's MFMAs),
-// instead of every wave reading them from L2. A key row's 16-byte piece s is
-// stored at position s ^ (row & 15), so the B-operand reads (16 consecutive
-// key rows, one piece each) hit all 64 banks.
+// d_idx = 128: 8 waves of 8 queries each (one 32-row A block, 32 q_idx
+// registers per wave, so that four waves fit per SIMD). The keys of a stage
+// (64 rows x 256 B) are read from global memory once per workgroup and shared
+// by its 8 waves through LDS (double buffered; the next stage's loads are in
+// flight during this stage's MFMAs), instead of every wave reading them from
+// L2. A key row's 16-byte piece s is stored at position s ^ (row & 15), so the
+// B-operand reads (16 consecutive key rows, one piece each) hit all 64 banks.
 constexpr int kIdxStageKeys = 64;
 constexpr int kIdxRowBytes = 256;  // 128 bf16
+constexpr int kIdx8Threads = 512;  // indexer_lds_kernel: 8 waves of 8 queries
 constexpr int kTbRow = 36;         // floats per row of a wave's score tile (32 keys + pad)
 
-__global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
+__global__ __launch_bounds__(kIdx8Threads) void indexer_lds_kernel(
     int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
     int n_units, int units_per_xcd, int keys_per_unit) {
@@ -202,9 +204,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
 
   __shared__ float sw[kIdxQueries][kIdxHeads];
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kIdxStageKeys * kIdxRowBytes];
-  __shared__ __attribute__((aligned(16))) float tbuf[kIdxThreads / 64][16 * kTbRow];
+  __shared__ __attribute__((aligned(16))) float tbuf[kIdx8Threads / 64][8 * kTbRow];
   const bool vec_ok = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
-  for (int e = threadIdx.x; e < kIdxQueries * kIdxHeads; e += kIdxThreads) {
+  for (int e = threadIdx.x; e < kIdxQueries * kIdxHeads; e += kIdx8Threads) {
     const int q = e >> 2;
     sw[q][e & 3] = (q < nrows) ? w[(int64_t)(q0 + q) * kIdxHeads + (e & 3)] : 0.0f;
   }
@@ -214,27 +216,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Stage loads: thread t copies pieces 4 (t % 4) .. +3 of key row t / 4.
-  const int ld_row = tid >> 2, ld_p0 = 4 * (tid & 3);
-  auto load_stage = [&](int st, u32x4 (&v)[4]) {
+  // Stage loads: thread t copies pieces 2 (t % 8), +1 of key row t / 8.
+  const int ld_row = tid >> 3, ld_p0 = 2 * (tid & 7);
+  auto load_stage = [&](int st, u32x4 (&v)[2]) {
     const int64_t key = k_begin + (int64_t)st * kIdxStageKeys + ld_row;
     const int64_t krow = key < t_ctx ? key : t_ctx - 1;  // clamped rows are masked later
     const u32x4* src = reinterpret_cast<const u32x4*>(k_idx + krow * D) + ld_p0;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) v[x] = src[x];
+    for (int x = 0; x < 2; ++x) v[x] = src[x];
   };
-  auto store_stage = [&](int buf, const u32x4 (&v)[4]) {
+  auto store_stage = [&](int buf, const u32x4 (&v)[2]) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < 2; ++x)
       *reinterpret_cast<u32x4*>(&kbuf[buf][ld_row * kIdxRowBytes + 16 * ((ld_p0 + x) ^ (ld_row & 15))]) = v[x];
   };
 
-  // A operand: rows (query, head) = 4*q + h of this wave's 16 queries, two
-  // 32-row blocks. Lane holds row l32, k-slice 8*hi .. 8*hi+7 of each k-step.
-  bf16x8 a[2][KS];
+  // A operand: rows (query, head) = 4*q + h of this wave's 8 queries, one
+  // 32-row block. Lane holds row l32, k-slice 8*hi .. 8*hi+7 of each k-step.
+  bf16x8 a[1][KS];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int qrow = wave * 16 + mb * 8 + (l32 >> 2);
+  for (int mb = 0; mb < 1; ++mb) {
+    const int qrow = wave * 8 + (l32 >> 2);
     const bool ok = qrow < nrows;
     const uint16_t* src = q_idx + ((int64_t)(q0 + (ok ? qrow : 0)) * kIdxHeads + (l32 & 3)) * D + 8 * hi;
 #pragma unroll
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
       a[mb][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  u32x4 pre[4];
+  u32x4 pre[2];
   load_stage(0, pre);
   store_stage(0, pre);
   __syncthreads();
@@ -263,9 +265,9 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
       for (int ks = 0; ks < KS; ++ks)
         b[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                &kb[krow * kIdxRowBytes + 16 * ((2 * ks + hi) ^ (krow & 15))]));
-      f32x16 acc[2];
+      f32x16 acc[1];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 1; ++mb) {
         acc[mb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -276,41 +278,41 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
       // negative int32); adding +0 turns a -0 sum into +0;
       // the causal mask is needed only where the block reaches the wave's
       // first query (block-uniform test).
-      const bool all_causal = nb + 31 <= (int64_t)offset + q0 + wave * 16;
-      const bool all_in = nb + 32 <= k_end && q0 + wave * 16 + 16 <= n_q;  // every row and key of the sub-block exists
+      const bool all_causal = nb + 31 <= (int64_t)offset + q0 + wave * 8;
+      const bool all_in = nb + 32 <= k_end && q0 + wave * 8 + 8 <= n_q;  // every row and key of the sub-block exists
       if (vec_ok && all_in) {
         // Through this wave's LDS tile, so that the stores are 16-byte vectors
         // (4 keys of one query per lane) instead of one score per lane.
         float* tb = tbuf[wave];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 1; ++mb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int qr = mb * 8 + 2 * g + hi;  // row inside the wave's 16 queries
+            const int qr = 2 * g + hi;  // row inside the wave's 8 queries
             float sc = 0.0f;
 #pragma unroll
             for (int h = 0; h < 4; ++h)
-              sc = fmaf(sw[wave * 16 + qr][h], __int_as_float(max(__float_as_int(acc[mb][4 * g + h]), 0)), sc);
+              sc = fmaf(sw[wave * 8 + qr][h], __int_as_float(max(__float_as_int(acc[mb][4 * g + h]), 0)), sc);
             sc = sc + 0.0f;
             if (!all_causal) {
-              const int64_t p = (int64_t)offset + q0 + wave * 16 + qr;
+              const int64_t p = (int64_t)offset + q0 + wave * 8 + qr;
               sc = key <= p ? sc : -INFINITY;
             }
             tb[qr * kTbRow + l32] = sc;
           }
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < 1; ++x) {
           const int piece = 64 * x + lane, r = piece >> 3, c = piece & 7;
           const f32x4 v = *reinterpret_cast<const f32x4*>(&tb[r * kTbRow + 4 * c]);
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(scores + (int64_t)(q0 + wave * 16 + r) * ld + nb + 4 * c));
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(scores + (int64_t)(q0 + wave * 8 + r) * ld + nb + 4 * c));
         }
         continue;
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 1; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int qrow = wave * 16 + mb * 8 + 2 * g + hi;
+          const int qrow = wave * 8 + 2 * g + hi;
           if (all_in || (qrow < nrows && key < k_end)) {
             float sc = 0.0f;
 #pragma unroll
@@ -336,6 +338,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_lds_kernel(
   if (written < k_end) fill_neg_inf(scores, ld, q0, nrows, written, k_end);
 }
 
+
 template <int D>
 hipError_t launch_mfma(const IndexerArgs& a, hipStream_t s) {
   const int n_qb = (a.n_q + kIdxQueries - 1) / kIdxQueries;
@@ -351,7 +354,7 @@ hipError_t launch_mfma(const IndexerArgs& a, hipStream_t s) {
   const int units_per_xcd = (int)((n_units + 7) / 8);
   const int grid = units_per_xcd * 8;
   if (D == 128 && kpu % kIdxStageKeys == 0) {
-    hipLaunchKernelGGL(indexer_lds_kernel, dim3(grid), dim3(kIdxThreads), 0, s, a.n_q, a.offset,
+    hipLaunchKernelGGL(indexer_lds_kernel, dim3(grid), dim3(kIdx8Threads), 0, s, a.n_q, a.offset,
                        static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx), a.scores,
                        a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
     return hipGetLastError();
