@@ -16,7 +16,10 @@
 //                  per-thread counts), so every later pass runs out of LDS;
 //   refine       : 1024-bin histograms of the next 10 and last 10 bits among
 //                  the keys of the boundary bucket -> exact threshold T and
-//                  r = number of keys equal to T that still fit;
+//                  r = number of keys equal to T that still fit; the second
+//                  is skipped when the last 10 bits agree over the whole
+//                  bucket (the first level's OR / AND of them), as they do
+//                  for integer-valued scores;
 //   emit         : in index order, keep key > T, and key == T while fewer
 //                  than r ties have been kept; the output position of a kept
 //                  key is (#greater before it) + min(#ties before it, r).
@@ -25,6 +28,7 @@
 // streamed twice from global memory, the next group's loads in flight while
 // the current group is counted. If the candidates do not fit in LDS, the
 // refine and emit passes re-read the row instead (same arithmetic).
+// Block scans run their wave part on DPP row shifts and broadcasts.
 #include "common.h"
 #include "kernels.h"
 
@@ -45,6 +49,7 @@ struct TopkSmem {
   int32_t cidx[kTkCap];
   uint64_t scan[2][kTkWaves];
   uint32_t bc[4];
+  uint32_t low_or, low_and;  // OR / AND of the boundary bucket's keys (last 10 bits)
 };
 
 // Barrier for LDS traffic only: unlike __syncthreads() it leaves this
@@ -56,18 +61,29 @@ __device__ __forceinline__ void lds_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Inclusive prefix sum over the wave with DPP moves: shifts of 1, 2, 4 and 8
+// lanes inside each row of 16, then row 0's total into row 1 and row 2's
+// into row 3 (row_bcast:15), then the total of rows 0-1 into rows 2-3
+// (row_bcast:31). Six dependent VALU steps instead of six LDS-crossbar
+// shuffles.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xa, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
 // Block-wide exclusive scan of a uint64 (callers pack independent counters in
 // bit fields that cannot overflow into each other). `buf` alternates between
 // calls so that a single barrier per scan suffices.
 __device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* total, TopkSmem& sm, int& buf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t lo = __shfl_up(static_cast<uint32_t>(x), o);
-    const uint32_t hi = __shfl_up(static_cast<uint32_t>(x >> 32), o);
-    if (lane >= o) x += (static_cast<uint64_t>(hi) << 32) | lo;
-  }
+  // The two 32-bit halves scan separately: no field carries across them.
+  const uint64_t x = (static_cast<uint64_t>(wave_incl_scan(static_cast<uint32_t>(v >> 32))) << 32) |
+                     wave_incl_scan(static_cast<uint32_t>(v));
   if (lane == kWave - 1) sm.scan[buf][wave] = x;
   lds_sync();
   uint64_t before = 0, all = 0;
@@ -113,6 +129,21 @@ __device__ __forceinline__ void select_bucket(TopkSmem& sm, int nbins, uint32_t 
   *cnt_out = sm.bc[2];
 }
 
+// Adds this wave's OR / AND of the last 10 bits of `o` / `a` to the
+// block's (one ballot per bit: no chain of dependent shuffles).
+__device__ __forceinline__ void publish_low_bits(TopkSmem& sm, uint32_t o, uint32_t a) {
+  uint32_t wo = 0u, wa = 0u;
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {
+    wo |= (__ballot((o >> b) & 1u) != 0) ? (1u << b) : 0u;
+    wa |= (__ballot(((a >> b) & 1u) == 0u) == 0) ? (1u << b) : 0u;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicOr(&sm.low_or, wo);
+    atomicAnd(&sm.low_and, wa);
+  }
+}
+
 // Loads elements base + 4*tid + e (e < 4) of the row; lanes past n get -inf.
 template <bool ALIGNED>
 __device__ __forceinline__ f32x4 load4(const float* __restrict__ row, int base, int n) {
@@ -147,10 +178,18 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
     for (int b = tid; b < kBins2; b += kTkThreads) sm.hist[b] = 0;
     __syncthreads();
     const int nshift = shift - 10;
+    // The first level also gathers the OR and the AND of the bucket's keys:
+    // where their last 10 bits agree over the whole bucket, the keys left
+    // after this level are all equal and the second level is not needed.
+    uint32_t lo = 0u, la = 0xFFFFFFFFu;
     if (in_lds) {
       for (int c = tid; c < n_cand; c += kTkThreads) {
         const uint32_t key = sm.ckey[c];
-        if ((key >> shift) == prefix) atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
+        if ((key >> shift) == prefix) {
+          atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
+          lo |= key;
+          la &= key;
+        }
       }
     } else {
       for (int base = 0; base < n; base += kSlice) {
@@ -158,10 +197,15 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = score_key(v[e]);
-          if (base + 4 * tid + e < n && (key >> shift) == prefix) atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
+          if (base + 4 * tid + e < n && (key >> shift) == prefix) {
+            atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
+            lo |= key;
+            la &= key;
+          }
         }
       }
     }
+    if (level == 0) publish_low_bits(sm, lo, la);
     __syncthreads();
     uint32_t b, above, cnt;
     select_bucket(sm, kBins2, need, &b, &above, &cnt, buf);
@@ -169,6 +213,11 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
     prefix = (prefix << 10) | b;
     shift = nshift;
     tie_cnt = cnt;
+    if (level == 0 && tie_cnt != need && ((sm.low_or ^ sm.low_and) & 1023u) == 0u) {
+      prefix = (prefix << 10) | (sm.low_or & 1023u);  // the single key value left
+      shift = 0;
+      break;
+    }
   }
   // Keys with (key >> shift) > prefix are kept; of those equal, the first `need`.
   const uint32_t r = need;
@@ -254,6 +303,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
 
   // ---- pass 1: histogram of the top 12 bits over the causal prefix.
   for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
+  if (tid == 0) {
+    sm.low_or = 0u;
+    sm.low_and = 0xFFFFFu;
+  }
   __syncthreads();
   // The loads of the next group go out before this group's atomics.
   f32x4 v[4];
@@ -328,8 +381,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
 // (thread t holds keys 2048 v + 4 t + e, all loads issued together), and
 // both the histogram and the ordered compaction run from those registers.
 template <int NV>
-__global__ __launch_bounds__(kTkThreads) void topk_reg_kernel(int offset, int k, const float* __restrict__ scores,
-                                                              int64_t ld, int32_t* __restrict__ idx) {
+__global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_reg_kernel(
+    int offset, int k, const float* __restrict__ scores, int64_t ld, int32_t* __restrict__ idx) {
   __shared__ TopkSmem sm;
   int buf = 0;
   const int i = blockIdx.x;
@@ -352,6 +405,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_reg_kernel(int offset, int k,
       for (int e = 0; e < 4; ++e) key[s][e] = score_key(v[s][e]);  // -inf past n: key 0x007FFFFF
   }
   for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
+  if (tid == 0) {
+    sm.low_or = 0u;
+    sm.low_and = 0xFFFFFu;
+  }
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < NV; ++s)
