@@ -45,8 +45,7 @@ constexpr int kTkCap = 6144;            // LDS candidate capacity
 
 struct TopkSmem {
   uint32_t hist[kBins1];
-  uint32_t ckey[kTkCap];
-  int32_t cidx[kTkCap];
+  u32x2 cand[kTkCap];  // (key, index) in index order
   uint64_t scan[2][kTkWaves];
   uint32_t bc[4];
   uint32_t low_or, low_and;  // OR / AND of the boundary bucket's keys (last 10 bits)
@@ -184,7 +183,7 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
     uint32_t lo = 0u, la = 0xFFFFFFFFu;
     if (in_lds) {
       for (int c = tid; c < n_cand; c += kTkThreads) {
-        const uint32_t key = sm.ckey[c];
+        const uint32_t key = sm.cand[c][0];
         if ((key >> shift) == prefix) {
           atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
           lo |= key;
@@ -233,8 +232,9 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
       for (int e = 0; e < 4; ++e) {
         const int c = base + 4 * tid + e;
         const bool valid = c < n_cand;
-        const uint32_t key = valid ? sm.ckey[c] : 0u;
-        jj[e] = valid ? sm.cidx[c] : -1;
+        const u32x2 kv = valid ? sm.cand[c] : u32x2{0u, 0xFFFFFFFFu};
+        const uint32_t key = kv[0];
+        jj[e] = static_cast<int32_t>(kv[1]);
         gt[e] = valid && (key >> shift) > prefix;
         tie[e] = valid && (key >> shift) == prefix;
         cgt += gt[e];
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
   const int tid = threadIdx.x;
 
   // ---- pass 1: histogram of the top 12 bits over the causal prefix.
-  for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
+  for (int b = 4 * tid; b < kBins1; b += 4 * kTkThreads) *reinterpret_cast<u32x4*>(&sm.hist[b]) = u32x4{0u, 0u, 0u, 0u};
   if (tid == 0) {
     sm.low_or = 0u;
     sm.low_and = 0xFFFFFu;
@@ -361,8 +361,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
         for (int e = 0; e < 4; ++e) {
           const int j = base + s * kSlice + 4 * tid + e;
           if (j < n && (key[s][e] >> 20) >= b1 && pos < static_cast<uint32_t>(kTkCap)) {
-            sm.ckey[pos] = key[s][e];
-            sm.cidx[pos] = j;
+            sm.cand[pos] = u32x2{key[s][e], static_cast<uint32_t>(j)};
             ++pos;
           }
         }
@@ -404,7 +403,7 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[s][e] = score_key(v[s][e]);  // -inf past n: key 0x007FFFFF
   }
-  for (int b = tid; b < kBins1; b += kTkThreads) sm.hist[b] = 0;
+  for (int b = 4 * tid; b < kBins1; b += 4 * kTkThreads) *reinterpret_cast<u32x4*>(&sm.hist[b]) = u32x4{0u, 0u, 0u, 0u};
   if (tid == 0) {
     sm.low_or = 0u;
     sm.low_and = 0xFFFFFu;
@@ -441,8 +440,7 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
         for (int e = 0; e < 4; ++e) {
           const int j = s * kSlice + 4 * tid + e;
           if (j < n && (key[s][e] >> 20) >= b1) {
-            sm.ckey[pos] = key[s][e];
-            sm.cidx[pos] = j;
+            sm.cand[pos] = u32x2{key[s][e], static_cast<uint32_t>(j)};
             ++pos;
           }
         }
