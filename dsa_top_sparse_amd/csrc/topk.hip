@@ -379,6 +379,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
 // Rows of at most NV * 2048 keys: the row is read once, into registers
 // (thread t holds keys 2048 v + 4 t + e, all loads issued together), and
 // both the histogram and the ordered compaction run from those registers.
+// Four waves per SIMD (at most 128 VGPRs) keep two rows in flight per CU;
+// a row's chain of block-wide steps is latency-bound, so the second row
+// nearly doubles the throughput.
 template <int NV>
 __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_reg_kernel(
     int offset, int k, const float* __restrict__ scores, int64_t ld, int32_t* __restrict__ idx) {
