@@ -75,11 +75,12 @@ def cpu_baseline(cfg, inputs, target_s: float):
     import numpy as np
     import oracle
     oracle.build(force=False)
-    spread = np.linspace(0, cfg.n_q - 1, 8).astype(int).tolist()
+    spread = np.linspace(0, cfg.n_q - 1, 16).astype(int).tolist()
+    oracle.full_path(cfg, inputs, rows=spread[:2])  # warm-up: thread pool, first-touch pages
     t0 = time.perf_counter()
     oracle.full_path(cfg, inputs, rows=spread)
     t_cal = time.perf_counter() - t0
-    n_rows = int(max(8, min(cfg.n_q, round(8 * target_s / max(t_cal, 1e-3)))))
+    n_rows = int(max(16, min(cfg.n_q, round(16 * target_s / max(t_cal, 1e-3)))))
     rows = np.linspace(0, cfg.n_q - 1, n_rows).astype(int).tolist()
     t0 = time.perf_counter()
     oracle.full_path(cfg, inputs, rows=rows)
