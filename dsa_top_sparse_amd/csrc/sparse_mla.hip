@@ -6,8 +6,9 @@
 // holding a key j with 0 <= j <= p:
 //   l_t = sm_scale * <q[i][h], kv[j]>   (all d_latent + d_rope dims)
 //   out[i][h] = sum_t softmax(l)_t * kv[j][0 : d_latent],  lse = log sum_t exp(l_t)
-// (feedman.me page: the "DSA sparse-attention core" attends each query to its
-// 2,048 gathered keys of the "512-wide latent KV"; the pages' own kernel runs
+// (feedman.me page, profile table row DSA sparse-attention core: each query
+// attends to the 2,048 keys it gathered from the per-token latent cache, whose
+// rows are 512 values wide; the pages' own kernel runs
 // one query per threadgroup with scalar dot products, and the same paragraph
 // proposes using the matrix units -- which is what the fast kernel below does.)
 //

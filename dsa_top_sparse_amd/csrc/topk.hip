@@ -3,9 +3,10 @@
 // For query i (absolute position p = offset + i) the causal scores are
 // scores[i][0 .. p]. If p + 1 <= k every causal key is kept; otherwise the k
 // keys first in (score descending, key index ascending) order are kept. The
-// kept indices are written ascending, padded with -1 to k. (feedman.me page:
-// "the per-query top-2048 gather kernel"; the tie rule is this library's
-// contract: a tie at the threshold goes to the lower key index.)
+// kept indices are written ascending, padded with -1 to k. (feedman.me page,
+// the paragraph on the work that is not a matmul: each query gathers its top
+// 2,048 keys; the tie rule is this library's contract: a tie at the
+// threshold goes to the lower key index.)
 //
 // One workgroup per query row, an exact radix select on the order-preserving
 // uint32 image of each score (12 + 10 + 10 bits):

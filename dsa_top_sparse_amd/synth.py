@@ -9,9 +9,10 @@ Workload shapes follow the feedman.me page ("GLM-5.3-Flash prefill on M5
 Ultra ..."): a prompt processed in 2,048- or 8,192-token chunks (its
 per-component profile table, "8,192 tokens in 2,048-token chunks", and the
 "Bigger prefill chunks" paragraph) against a cache of earlier tokens with a
-512-wide latent KV per token ("Why the hand-off is cheap"), and a per-query
-top-2,048 selection ("the per-query top-2048 gather kernel"). The 17.5k-token
-prompt of the same page sets the 17,536-token context of one workload.
+latent KV row of 512 values per token ("Why the hand-off is cheap"), and a
+top-2,048 selection per query (the paragraph on the work that is not a
+matmul). The 17.5k-token prompt of the same page sets the 17,536-token context
+of one workload.
 
 Distributions (the pages give none; fixed here so that both sides agree):
   * q and the latent cache kv: fp32 N(0, 1) draws, rounded to bf16

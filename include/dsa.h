@@ -15,7 +15,7 @@
  * sparse-attention core"; the paragraph on what is not a matmul names the
  * per-query top-2,048 gather; the paragraph on the sparse-attention kernel
  * describes one query gathering its 2,048 keys; the hand-off paragraph gives
- * the 512-wide latent KV per token. The pages print no formula, so the exact
+ * each token a latent KV row of 512 values. The pages print no formula, so the exact
  * definitions below are this library's contract (the same definitions as the
  * CPU oracle it is tested against).
  *

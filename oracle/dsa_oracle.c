@@ -16,21 +16,23 @@
  *      for 0 <= j <= p_i, and -inf for p_i < j < ld.  Accumulated in fp64,
  *      rounded once to fp32; a zero score is written as +0.0.
  *
- *   2. Per-query top-k selection (same page: "the per-query top-2048 gather
- *      kernel"): if p_i + 1 <= k every causal key is kept; otherwise the keys
+ *   2. Per-query top-k selection (same page, the paragraph on the work that
+ *      is not a matmul: each query gathers the 2,048 keys it selected): if p_i + 1 <= k every causal key is kept; otherwise the keys
  *      are sorted by score descending, then by key index ascending (lower
  *      index wins a tie), and the first k are kept. The kept indices are
  *      written in ascending order and padded with -1 up to k.
  *
- *   3. Sparse attention over the kept keys (same page: "DSA sparse-attention
- *      core" on a "512-wide latent KV"): for each head h,
+ *   3. Sparse attention over the kept keys (same page: the profile table's
+ *      DSA sparse-attention core row; its hand-off paragraph gives each token
+ *      a latent KV row 512 values wide): for each head h,
  *          l_j  = sm_scale * sum_{d < d_qk} q[i][h][d] * kv[j][d]
  *          o[c] = sum_j softmax(l)_j * kv[j][c]     for c < d_v
  *          lse  = log(sum_j exp(l_j))
  *      over the slots j of the row with 0 <= j <= p_i (other slots, such as
  *      the -1 padding, are ignored). A row with no valid slot gives o = 0 and
- *      lse = -inf. All arithmetic in fp64 (page 5, "Prompt speed": changed
- *      reduction orders are checked against FP64 references).
+ *      lse = -inf. All arithmetic in fp64 (TensorFold issue #743, "Proposal:
+ *      restore single-Mac GLM-5.3-Flash on the M3 Ultra": kernels that change
+ *      the order of a reduction are validated against fp64 references).
  *
  * Inputs of dtype code 0 are bf16 bit patterns (uint16), widened exactly; code
  * 1 is fp32. Every function takes an optional list of query rows to compute
