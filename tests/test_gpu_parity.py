@@ -223,6 +223,32 @@ def test_topk_random_floats_and_negative_zero(torch_cuda):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("off", [9000, 30000])
+def test_topk_constant_low_bits(torch_cuda, off):
+    # Scores 1 + m/8 + 2^-20 (m random in [0, 8)): every score has the same
+    # exponent and the same nonzero low mantissa bits, so the select's second
+    # refinement level is skipped with a threshold whose last bits are not 0;
+    # and 2 + m/8 (low bits 0). Register and streaming kernels, vs the oracle.
+    torch = torch_cuda
+    rng = np.random.default_rng(off)
+    n_q, k = 12, 2048
+    ld = off + n_q
+    m = rng.integers(0, 8, size=(n_q, ld)).astype(np.float64)
+    s = (1.0 + m / 8 + 2.0 ** -20).astype(np.float32)
+    s[1::2] = (2.0 + m[1::2] / 8).astype(np.float32)
+    assert np.all(s[0].view(np.uint32) & 0x3FF == s[0, 0].view(np.uint32) & 0x3FF)
+    for i in range(n_q):
+        s[i, off + i + 1:] = -np.inf
+    _say(f"topk constant low bits: offset={off}")
+    st = torch.from_numpy(s).cuda()
+    idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
+    binding.topk_select(binding.make_dims(cfg), st, ld, idx)
+    torch.cuda.synchronize()
+    ref = oracle.topk_select(n_q, off, k, s)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("off,k,ld_pad", [(7000, 2048, 0), (30000, 2048, 4), (60000, 1500, 0), (70000, 2048, 0),
                                           (5000, 999, 1)])
 def test_topk_row_lengths(torch_cuda, off, k, ld_pad):
