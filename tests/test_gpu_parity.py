@@ -223,6 +223,32 @@ def test_topk_random_floats_and_negative_zero(torch_cuda):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("shape", [
+    # (n_heads, d_latent, d_rope, n_idx_heads, d_idx, top_k): which kernels run
+    (16, 128, 32, 4, 64, 96),    # MFMA indexer for d_idx 64; plain attention in bf16
+    (64, 512, 64, 4, 256, 130),  # MFMA indexer for d_idx 256; top_k % 4 != 0: plain attention
+    (8, 64, 0, 2, 48, 50),       # plain indexer in bf16 (2 heads, width 48); plain attention
+    (64, 512, 64, 4, 32, 64),    # MFMA indexer for d_idx 32; fast attention with a short index row
+])
+def test_other_shapes_bf16(torch_cuda, shape):
+    # Every step on bf16 inputs whose shapes leave the 4 x 128 indexer and the
+    # 64-head 512 + 64 attention: scores and indices bit-exact, attention
+    # within tolerance, every row against the oracle.
+    torch = torch_cuda
+    h, dl, dr, hi_, di, k = shape
+    cfg = synth.CONFIGS["C2"].replace(name=f"shape{shape}", n_q=70, offset=301, n_heads=h, d_latent=dl,
+                                      d_rope=dr, n_idx_heads=hi_, d_idx=di, top_k=k, seed=sum(shape))
+    inputs = synth.generate(cfg)
+    _say(f"other shape: {shape}")
+    dev, outs = run_gpu(torch, cfg, inputs)
+    ref = oracle.full_path(cfg, inputs)
+    assert np.array_equal(outs["scores"][:, : cfg.t_ctx].cpu().numpy().view(np.uint32),
+                          oracle.indexer_scores(cfg.n_q, cfg.offset, inputs["qidx"], inputs["w"],
+                                                inputs["kidx"]).view(np.uint32))
+    assert np.array_equal(outs["idx"].cpu().numpy(), ref["idx"])
+    check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], f"{shape}")
+
+
 @pytest.mark.parametrize("off", [9000, 30000])
 def test_topk_constant_low_bits(torch_cuda, off):
     # Scores 1 + m/8 + 2^-20 (m random in [0, 8)): every score has the same
