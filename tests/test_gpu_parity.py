@@ -249,6 +249,29 @@ def test_other_shapes_bf16(torch_cuda, shape):
     check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], f"{shape}")
 
 
+@pytest.mark.parametrize("off,k", [(12000, 4096), (12000, 9000), (40000, 10000)])
+def test_topk_large_k(torch_cuda, off, k):
+    # k above the select's LDS candidate capacity (6,144): the refinement and
+    # the emit re-read the row from global memory, in both select kernels;
+    # integer-valued scores with ties on even rows, random floats on odd rows.
+    torch = torch_cuda
+    rng = np.random.default_rng(off + k)
+    n_q = 8
+    ld = off + n_q
+    s = rng.integers(0, 200, size=(n_q, ld)).astype(np.float32)
+    s[1::2] = rng.standard_normal((n_q // 2, ld)).astype(np.float32)
+    for i in range(n_q):
+        s[i, off + i + 1:] = -np.inf
+    _say(f"topk large k: offset={off} k={k}")
+    st = torch.from_numpy(s).cuda()
+    idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
+    binding.topk_select(binding.make_dims(cfg), st, ld, idx)
+    torch.cuda.synchronize()
+    ref = oracle.topk_select(n_q, off, k, s)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("off", [9000, 30000])
 def test_topk_constant_low_bits(torch_cuda, off):
     # Scores 1 + m/8 + 2^-20 (m random in [0, 8)): every score has the same
