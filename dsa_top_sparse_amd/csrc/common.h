@@ -22,18 +22,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// Two fp32 -> packed bf16x2 (lo in bits 0..15).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-}
-
 // Order-preserving map of an fp32 score to uint32: a > b (as floats) iff
 // key(a) > key(b). -0.0 is folded onto +0.0 first so that the two compare
 // equal, as they do as floats.
@@ -42,16 +30,6 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-
-__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
-
-// Number of set bits of `mask` in lanes below the calling lane.
-__device__ __forceinline__ int lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-}
-
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -75,19 +53,6 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
-}
-
-// Exclusive prefix sum over the wave (lane order) and the wave total.
-__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
-  int x = v;
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (l >= o) x += y;
-  }
-  *total = __shfl(x, kWave - 1);
-  return x - v;
 }
 
 }  // namespace dsa

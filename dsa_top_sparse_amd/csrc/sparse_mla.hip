@@ -156,8 +156,6 @@ __device__ __forceinline__ float sum_over_q4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ bool slot_valid(int32_t j, int64_t p) { return j >= 0 && (int64_t)j <= p; }
-
 // Two fp32 -> packed bf16 pair (round to nearest even, hardware conversion).
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
