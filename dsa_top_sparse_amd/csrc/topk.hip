@@ -26,9 +26,13 @@
 //                  key is (#greater before it) + min(#ties before it, r).
 // Rows of at most 16,384 keys (topk_reg_kernel) are read once, into
 // registers, and both passes run from there. Longer rows (topk_kernel) are
-// streamed twice from global memory, the next group's loads in flight while
-// the current group is counted. If the candidates do not fit in LDS, the
-// refine and emit passes re-read the row instead (same arithmetic).
+// streamed: the histogram of their first 8,192 keys gives a speculative
+// bucket bs a margin below the k-th key's expected place, and one pass then
+// builds the full histogram while it compacts every key with top bits >= bs;
+// if the exact bucket b1 turns out >= bs and those keys fit in LDS, the row
+// is read once, else a second pass compacts the keys >= b1. If the
+// candidates do not fit in LDS, the refine and emit passes re-read the row
+// instead (same arithmetic).
 // Block scans run their wave part on DPP row shifts and broadcasts.
 #include "common.h"
 #include "kernels.h"
@@ -165,9 +169,8 @@ __device__ __forceinline__ f32x4 load4(const float* __restrict__ row, int base, 
 template <bool ALIGNED>
 __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float* __restrict__ row, int n, int k,
                                             int32_t* __restrict__ out, uint32_t b1, uint32_t above1, uint32_t cnt1,
-                                            bool in_lds) {
+                                            bool in_lds, int n_cand) {
   const int tid = threadIdx.x;
-  const int n_cand = static_cast<int>(above1 + cnt1);
 
   // ---- refine: exact threshold inside bucket b1 with two 10-bit digits.
   uint32_t need = static_cast<uint32_t>(k) - above1;
@@ -302,41 +305,108 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
   const float* __restrict__ row = scores + static_cast<int64_t>(i) * ld;
   const int tid = threadIdx.x;
 
-  // ---- pass 1: histogram of the top 12 bits over the causal prefix.
+  // ---- histogram of group 0 (keys 0 .. 8,191), which stays in registers.
   for (int b = 4 * tid; b < kBins1; b += 4 * kTkThreads) *reinterpret_cast<u32x4*>(&sm.hist[b]) = u32x4{0u, 0u, 0u, 0u};
   if (tid == 0) {
     sm.low_or = 0u;
     sm.low_and = 0xFFFFFu;
   }
   __syncthreads();
-  // The loads of the next group go out before this group's atomics.
-  f32x4 v[4];
+  f32x4 v[4], nx[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) v[s] = load4<ALIGNED>(row, s * kSlice, n);
-  for (int base = 0; base < n; base += 4 * kSlice) {
-    f32x4 nx[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) nx[s] = load4<ALIGNED>(row, base + 4 * kSlice + s * kSlice, n);
+  for (int s = 0; s < 4; ++s) nx[s] = load4<ALIGNED>(row, 4 * kSlice + s * kSlice, n);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[score_key(v[s][e]) >> 20], 1u);
+  __syncthreads();
+
+  // ---- speculative candidate bucket bs: where group 0 reaches a rank a
+  // quarter above the k-th key's expected rank in it. If the exact bucket b1
+  // found below is >= bs and the keys with top bits >= bs fit in LDS, the one
+  // pass below has already compacted every key the select needs (and some
+  // more, which the refine and emit steps pass over); else the row is read
+  // a second time, as in the plain two-pass select.
+  const int n0 = min(n, 4 * kSlice);
+  uint32_t need_s = static_cast<uint32_t>((static_cast<int64_t>(k) * n0 + n - 1) / n);
+  need_s += need_s / 4 + 64;
+  const bool spec = n > 4 * kSlice && need_s <= static_cast<uint32_t>(n0);
+  uint32_t bs = 0;
+  if (spec) {
+    uint32_t a_s, c_s;
+    select_bucket(sm, kBins1, need_s, &bs, &a_s, &c_s, buf);
+  }
+
+  // ---- one pass: the histogram of groups 1.. and, when speculating, the
+  // ordered compaction of every key with top bits >= bs. The loads of the
+  // group after next go out before this group is counted.
+  uint32_t cbase = 0;
+  for (int base = 0; base < n; base += 4 * kSlice) {
+    f32x4 nn[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) nn[s] = load4<ALIGNED>(row, base + 8 * kSlice + s * kSlice, n);
+    uint32_t key[4][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (base + s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[score_key(v[s][e]) >> 20], 1u);
+      for (int e = 0; e < 4; ++e) key[s][e] = score_key(v[s][e]);
+    if (base > 0) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) v[s] = nx[s];
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (base + s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[key[s][e] >> 20], 1u);
+    }
+    if (spec) {
+      uint64_t packed = 0;  // 4 x 16-bit per-slice counts (each slice total <= 2048)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += (base + s * kSlice + 4 * tid + e < n) && (key[s][e] >> 20) >= bs;
+        packed |= static_cast<uint64_t>(c) << (16 * s);
+      }
+      uint64_t tot;
+      const uint64_t excl = block_excl_scan(packed, &tot, sm, buf);
+      uint32_t slice_base = cbase;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t pos = slice_base + static_cast<uint32_t>((excl >> (16 * s)) & 0xFFFF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = base + s * kSlice + 4 * tid + e;
+          if (j < n && (key[s][e] >> 20) >= bs && pos < static_cast<uint32_t>(kTkCap)) {
+            sm.cand[pos] = u32x2{key[s][e], static_cast<uint32_t>(j)};
+            ++pos;
+          }
+        }
+        slice_base += static_cast<uint32_t>((tot >> (16 * s)) & 0xFFFF);
+      }
+      cbase = slice_base;  // every key >= bs so far, also those past the capacity
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v[s] = nx[s];
+      nx[s] = nn[s];
+    }
   }
   __syncthreads();
   uint32_t b1, above1, cnt1;
   select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
-  const bool in_lds = above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
+  const bool spec_ok = spec && b1 >= bs && cbase <= static_cast<uint32_t>(kTkCap);
+  const bool in_lds = spec_ok || above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
+  int n_cand = static_cast<int>(spec_ok ? cbase : above1 + cnt1);
 
-  // ---- pass 2: ordered compaction of every key with top bits >= b1 into LDS.
-  if (in_lds) {
-    uint32_t cbase = 0;
+  // ---- second read (speculation missed): ordered compaction of every key
+  // with top bits >= b1 into LDS.
+  if (in_lds && !spec_ok) {
+    cbase = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) v[s] = load4<ALIGNED>(row, s * kSlice, n);
     for (int base = 0; base < n; base += 4 * kSlice) {
-      f32x4 nx[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) nx[s] = load4<ALIGNED>(row, base + 4 * kSlice + s * kSlice, n);
       uint32_t key[4][4];
@@ -372,9 +442,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
 #pragma unroll
       for (int s = 0; s < 4; ++s) v[s] = nx[s];
     }
-    __syncthreads();
   }
-  select_tail<ALIGNED>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds);
+  __syncthreads();
+  select_tail<ALIGNED>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds, n_cand);
 }
 
 // Rows of at most NV * 2048 keys: the row is read once, into registers
@@ -454,7 +524,7 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
     __syncthreads();
   }
-  select_tail<true>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds);
+  select_tail<true>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds, static_cast<int>(above1 + cnt1));
 }
 
 }  // namespace

@@ -249,6 +249,39 @@ def test_other_shapes_bf16(torch_cuda, shape):
     check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], f"{shape}")
 
 
+@pytest.mark.parametrize("order", ["increasing", "decreasing", "random"])
+def test_topk_long_rows_speculation(torch_cuda, order):
+    # Rows past 16,384 keys take the streaming select, which guesses a
+    # candidate bucket from each row's first 8,192 keys. Increasing scores make
+    # the guess far too low (the candidates overflow LDS), decreasing scores
+    # make it too high (the k-th key lies below it); both must fall back to a
+    # second read. Random integer scores take the one-pass path. Ties at
+    # several places; every row against the oracle.
+    torch = torch_cuda
+    rng = np.random.default_rng(len(order))
+    n_q, off, k = 10, 30000, 2048
+    ld = off + n_q
+    j = np.arange(ld, dtype=np.float64)
+    if order == "increasing":
+        base = np.floor(j / 3)
+    elif order == "decreasing":
+        base = ld - j  # the k-th key's bucket lies below the guessed one
+    else:
+        base = rng.integers(0, 400, size=ld).astype(np.float64)
+    s = np.tile(base, (n_q, 1)).astype(np.float32)
+    s[:, 5000:5100] = s[0, 5000]  # a block of equal scores
+    for i in range(n_q):
+        s[i, off + i + 1:] = -np.inf
+    _say(f"topk long rows: {order}")
+    st = torch.from_numpy(s).cuda()
+    idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
+    binding.topk_select(binding.make_dims(cfg), st, ld, idx)
+    torch.cuda.synchronize()
+    ref = oracle.topk_select(n_q, off, k, s)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("off,k", [(12000, 4096), (12000, 9000), (40000, 10000)])
 def test_topk_large_k(torch_cuda, off, k):
     # k above the select's LDS candidate capacity (6,144): the refinement and
