@@ -127,7 +127,7 @@ __device__ __forceinline__ void select_bucket(TopkSmem& sm, int nbins, uint32_t 
       run += h;
     }
   }
-  __syncthreads();
+  lds_sync();  // LDS only: loads of the streaming select stay in flight
   *b_out = sm.bc[0];
   *above_out = sm.bc[1];
   *cnt_out = sm.bc[2];
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[score_key(v[s][e]) >> 20], 1u);
-  __syncthreads();
+  lds_sync();  // the loads of group 1 stay in flight
 
   // ---- speculative candidate bucket bs: where group 0 reaches a rank a
   // quarter above the k-th key's expected rank in it. If the exact bucket b1
