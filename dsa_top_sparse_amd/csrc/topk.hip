@@ -24,8 +24,8 @@
 //   emit         : in index order, keep key > T, and key == T while fewer
 //                  than r ties have been kept; the output position of a kept
 //                  key is (#greater before it) + min(#ties before it, r).
-// Rows of at most 16,384 keys (topk_reg_kernel) are read once, into
-// registers, and both passes run from there. Longer rows (topk_kernel) are
+// Rows of at most 18,432 keys (topk_reg_kernel, 32 or 36 keys per thread)
+// are read once, into registers, and both passes run from there. Longer rows (topk_kernel) are
 // streamed: the histogram of their first 8,192 keys gives a speculative
 // bucket bs a margin below the k-th key's expected place, and one pass then
 // builds the full histogram while it compacts every key with top bits >= bs;
@@ -535,6 +535,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   const int64_t n_max = (int64_t)a.offset + a.n_q;  // longest causal row
   if (aligned && n_max <= 8 * kSlice)
     hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores, a.ld,
+                       a.idx);
+  else if (aligned && n_max <= 9 * kSlice)
+    hipLaunchKernelGGL(topk_reg_kernel<9>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores, a.ld,
                        a.idx);
   else if (aligned)
     hipLaunchKernelGGL(topk_kernel<true>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores,

@@ -331,7 +331,8 @@ def test_topk_constant_low_bits(torch_cuda, off):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("off,k,ld_pad", [(7000, 2048, 0), (30000, 2048, 4), (60000, 1500, 0), (70000, 2048, 0),
+@pytest.mark.parametrize("off,k,ld_pad", [(7000, 2048, 0), (17000, 2048, 0), (30000, 2048, 4), (60000, 1500, 0),
+                                          (70000, 2048, 0),
                                           (5000, 999, 1)])
 def test_topk_row_lengths(torch_cuda, off, k, ld_pad):
     # Row lengths across every register-resident variant of the select (up to
