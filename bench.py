@@ -166,7 +166,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C3", help="workload id C0..C4 (default: 8k chunk at offset 8k)")
     ap.add_argument("--cold", action="store_true", help="overwrite a 1 GiB buffer before each step (MALL/L2 flush)")
-    ap.add_argument("--cpu-baseline-s", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--cpu-baseline-s", type=float, default=18.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-replay", dest="replay", action="store_false",
                     help="skip the side measurements: chunked-prefill replay (8,192 tokens from empty caches in "
                          "2,048-token chunks) and decode steps")
