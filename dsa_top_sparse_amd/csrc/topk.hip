@@ -59,10 +59,9 @@ struct TopkSmem {
 // Barrier for LDS traffic only: unlike __syncthreads() it leaves this
 // thread's global loads in flight (the streaming passes prefetch across it).
 __device__ __forceinline__ void lds_sync() {
-  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Inclusive prefix sum over the wave with DPP moves: shifts of 1, 2, 4 and 8
@@ -148,13 +147,16 @@ __device__ __forceinline__ void publish_low_bits(TopkSmem& sm, uint32_t o, uint3
   }
 }
 
-// Loads elements base + 4*tid + e (e < 4) of the row; lanes past n get -inf.
+// Loads elements base + 4*tid + e (e < 4) of the row. Elements past n hold
+// unspecified values: every user tests e < n itself. The aligned load is not
+// predicated (its address is clamped into the row), so the compiler can wait
+// for each load separately instead of for all loads in flight.
 template <bool ALIGNED>
 __device__ __forceinline__ f32x4 load4(const float* __restrict__ row, int base, int n) {
   const int j = base + 4 * threadIdx.x;
   f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   if (ALIGNED) {
-    if (j < n) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + j));
+    v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + min(j, (n - 1) & ~3)));
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -468,27 +470,26 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const float* __restrict__ row = scores + static_cast<int64_t>(i) * ld;
   const int tid = threadIdx.x;
   uint32_t key[NV][4];
-  {
-    f32x4 v[NV];
+  f32x4 v[NV];
 #pragma unroll
-    for (int s = 0; s < NV; ++s) v[s] = load4<true>(row, s * kSlice, n);
-#pragma unroll
-    for (int s = 0; s < NV; ++s)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) key[s][e] = score_key(v[s][e]);  // -inf past n: key 0x007FFFFF
+  for (int s = 0; s < NV; ++s) {
+    v[s] = load4<true>(row, s * kSlice, n);
   }
   for (int b = 4 * tid; b < kBins1; b += 4 * kTkThreads) *reinterpret_cast<u32x4*>(&sm.hist[b]) = u32x4{0u, 0u, 0u, 0u};
   if (tid == 0) {
     sm.low_or = 0u;
     sm.low_and = 0xFFFFFu;
   }
-  __syncthreads();
+  lds_sync();  // the row's loads stay in flight: each slice is counted as it lands
 #pragma unroll
-  for (int s = 0; s < NV; ++s)
+  for (int s = 0; s < NV; ++s) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
+      key[s][e] = score_key(v[s][e]);  // lanes past n: masked below and in the compaction
       if (s * kSlice + 4 * tid + e < n) atomicAdd(&sm.hist[key[s][e] >> 20], 1u);
-  __syncthreads();
+    }
+  }
+  lds_sync();
   uint32_t b1, above1, cnt1;
   select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
   const bool in_lds = above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
