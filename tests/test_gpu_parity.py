@@ -332,13 +332,14 @@ def test_topk_constant_low_bits(torch_cuda, off):
 
 
 @pytest.mark.parametrize("off,k,ld_pad", [(7000, 2048, 0), (17000, 2048, 0), (30000, 2048, 4), (60000, 1500, 0),
-                                          (70000, 2048, 0),
-                                          (5000, 999, 1)])
+                                          (70000, 2048, 0), (5000, 999, 1),
+                                          (16368, 2048, 0), (16369, 2048, 0), (18416, 2048, 0), (18417, 2048, 0)])
 def test_topk_row_lengths(torch_cuda, off, k, ld_pad):
-    # Row lengths across every register-resident variant of the select (up to
-    # 65,536 keys per row), the global-memory variant beyond, and an unaligned
-    # leading dimension; integer-valued scores with many ties plus random
-    # floats, vs the oracle.
+    # Row lengths in both register-resident kernels (32 and 36 keys per thread:
+    # rows of up to 16,384 and 18,432 keys, each limit hit exactly and passed
+    # by one key), the streamed kernel beyond (up to 70,016 keys), and
+    # unaligned leading dimensions; integer-valued scores with many ties plus
+    # random floats, vs the oracle.
     torch = torch_cuda
     rng = np.random.default_rng(off + k)
     n_q = 16
