@@ -12,6 +12,7 @@ import sys
 import numpy as np
 import pytest
 
+import golden_cases
 import oracle
 from dsa_top_sparse_amd import binding, synth
 
@@ -547,3 +548,47 @@ def test_attention_reference_restart(torch_cuda):
     ref_o, ref_l = oracle.sparse_mla(cfg.n_q, cfg.offset, cfg.sm_scale, cfg.d_latent, inputs["q"], inputs["kv"], idx)
     assert ref_l[0, 5] > 55.0  # the planted logit dominates head 5
     check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "restart")
+
+
+def test_golden_fixtures_through_the_abi(torch_cuda):
+    # The hand-worked fixtures of tests/golden (fp32 inputs, so the general
+    # kernels run) through the C ABI: scores and indices exact, attention to
+    # fp32 rounding. Each top-k case runs at its own (unaligned) leading
+    # dimension and padded with -inf to a multiple of 4, so both the streamed
+    # and the register-resident select see it.
+    torch = torch_cuda
+    F32 = binding.DSA_F32
+    _say("golden fixtures")
+    g = golden_cases.load("indexer_hand.json")
+    q_idx = torch.from_numpy(golden_cases.array(g["q_idx"])).cuda()
+    n_h, d_i = q_idx.shape[1], q_idx.shape[2]
+    dims = binding.Dims(g["n_q"], g["offset"], 1, 1, 0, n_h, d_i, 1, 1.0, F32, F32)
+    scores = torch.full((g["n_q"], g["ld"]), 7.0, dtype=torch.float32, device="cuda")
+    binding.indexer_scores(dims, q_idx, torch.from_numpy(golden_cases.array(g["w_idx"])).cuda(),
+                           torch.from_numpy(golden_cases.array(g["k_idx"])).cuda(), scores, g["ld"])
+    torch.cuda.synchronize()
+    got, want = scores.cpu().numpy(), golden_cases.array(g["scores"])
+    assert np.array_equal(got, want) and np.array_equal(np.signbit(got), np.signbit(want))
+
+    for case in golden_cases.load("topk_hand.json")["cases"]:
+        s = golden_cases.array(case["scores"])
+        for ld in (s.shape[1], (s.shape[1] + 3) // 4 * 4):
+            sp = np.full((case["n_q"], ld), -np.inf, dtype=np.float32)
+            sp[:, : s.shape[1]] = s
+            dims = binding.Dims(case["n_q"], case["offset"], 1, 1, 0, 1, 1, case["k"], 1.0, F32, F32)
+            idx = torch.full((case["n_q"], case["k"]), 12345, dtype=torch.int32, device="cuda")
+            binding.topk_select(dims, torch.from_numpy(sp).cuda(), ld, idx)
+            torch.cuda.synchronize()
+            assert idx.cpu().tolist() == case["idx"], (case["offset"], ld)
+
+    g = golden_cases.load("attention_hand.json")
+    dims = binding.Dims(g["n_q"], g["offset"], g["n_heads"], g["d_latent"], g["d_rope"], 1, 1,
+                        len(g["idx"][0]), g["sm_scale"], F32, F32)
+    out = torch.full((g["n_q"], g["n_heads"], g["d_latent"]), 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full((g["n_q"], g["n_heads"]), 7.0, dtype=torch.float32, device="cuda")
+    binding.sparse_mla_fwd(dims, torch.from_numpy(golden_cases.array(g["q"])).cuda(),
+                           torch.from_numpy(golden_cases.array(g["kv"])).cuda(),
+                           torch.from_numpy(golden_cases.array(g["idx"], np.int32)).cuda(), out, lse)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(out.cpu().numpy() - np.array(g["out"]))) < g["tol"]
+    assert np.max(np.abs(lse.cpu().numpy() - np.array(g["lse"]))) < g["tol"]

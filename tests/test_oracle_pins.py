@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 from scipy.special import logsumexp
 
+import golden_cases
 import oracle
 from dsa_top_sparse_amd import synth
 
@@ -331,3 +332,30 @@ def test_attention_bf16_widening_exact(oracle_lib):
     assert np.array_equal(a, b)
     ref, _ = _numpy_attention(d["q"][7], d["kv"], idx[0], cfg.sm_scale, cfg.d_latent)
     assert np.max(np.abs(a[0] - ref)) < 1e-13
+
+
+# ---------------------------------------------------------------- hand-worked fixtures (tests/golden)
+
+
+def test_golden_indexer_hand(oracle_lib):
+    g = golden_cases.load("indexer_hand.json")
+    s = oracle.indexer_scores(g["n_q"], g["offset"], golden_cases.array(g["q_idx"]),
+                              golden_cases.array(g["w_idx"]), golden_cases.array(g["k_idx"]), ld=g["ld"])
+    want = golden_cases.array(g["scores"])
+    assert np.array_equal(s, want)
+    assert np.array_equal(np.signbit(s), np.signbit(want))  # zero scores are +0.0
+
+
+def test_golden_topk_hand(oracle_lib):
+    for case in golden_cases.load("topk_hand.json")["cases"]:
+        s = golden_cases.array(case["scores"])
+        got = oracle.topk_select(case["n_q"], case["offset"], case["k"], s)
+        assert got.tolist() == case["idx"]
+
+
+def test_golden_attention_hand(oracle_lib):
+    g = golden_cases.load("attention_hand.json")
+    out, lse = oracle.sparse_mla(g["n_q"], g["offset"], g["sm_scale"], g["d_latent"], golden_cases.array(g["q"]),
+                                 golden_cases.array(g["kv"]), golden_cases.array(g["idx"], np.int32))
+    assert np.max(np.abs(out - np.array(g["out"]))) < 1e-12
+    assert np.max(np.abs(lse - np.array(g["lse"]))) < 1e-12
