@@ -51,6 +51,7 @@ constexpr int kTkCap = 6144;            // LDS candidate capacity
 struct TopkSmem {
   uint32_t hist[kBins1];
   u32x2 cand[kTkCap];  // (key, index) in index order
+  uint32_t hist2[kBins2];  // the first refinement's histogram when the compaction builds it
   uint64_t scan[2][kTkWaves];
   uint32_t bc[4];
   uint32_t low_or, low_and;  // OR / AND of the boundary bucket's keys (last 10 bits)
@@ -104,19 +105,20 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* total,
 // Finds the bucket b (scanning from the top bin down) at which the running
 // count of keys reaches `need`; returns b and the count strictly above it.
 // Requires that the histogram holds at least `need` keys.
-__device__ __forceinline__ void select_bucket(TopkSmem& sm, int nbins, uint32_t need, uint32_t* b_out,
+__device__ __forceinline__ void select_bucket(const uint32_t* hist, TopkSmem& sm, int nbins, uint32_t need,
+                                              uint32_t* b_out,
                                               uint32_t* above_out, uint32_t* cnt_out, int& buf) {
   const int per = nbins / kTkThreads;
   const int lo = threadIdx.x * per;
   uint32_t local = 0;
-  for (int b = 0; b < per; ++b) local += sm.hist[lo + b];
+  for (int b = 0; b < per; ++b) local += hist[lo + b];
   uint64_t total;
   const uint64_t excl = block_excl_scan(local, &total, sm, buf);
   const uint32_t above = static_cast<uint32_t>(total - excl - local);  // keys in higher bins
   if (above < need && above + local >= need) {
     uint32_t run = above;
     for (int b = lo + per - 1; b >= lo; --b) {
-      const uint32_t h = sm.hist[b];
+      const uint32_t h = hist[b];
       if (run + h >= need) {
         sm.bc[0] = b;
         sm.bc[1] = run;
@@ -167,11 +169,13 @@ __device__ __forceinline__ f32x4 load4(const float* __restrict__ row, int base, 
 
 // Refine and emit, after bucket b1 (holding the k-th largest key; above1 keys
 // lie in higher buckets, cnt1 in b1) is known and, when in_lds, the keys with
-// top bits >= b1 sit in LDS in index order.
+// top bits >= b1 sit in LDS in index order. With level0_built the compaction
+// has already built the first refinement's histogram in sm.hist2 and
+// published the OR / AND of the bucket's last 10 bits.
 template <bool ALIGNED>
 __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float* __restrict__ row, int n, int k,
                                             int32_t* __restrict__ out, uint32_t b1, uint32_t above1, uint32_t cnt1,
-                                            bool in_lds, int n_cand) {
+                                            bool in_lds, int n_cand, bool level0_built) {
   const int tid = threadIdx.x;
 
   // ---- refine: exact threshold inside bucket b1 with two 10-bit digits.
@@ -180,40 +184,43 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
   int shift = 20;        // number of undecided low bits
   uint32_t tie_cnt = cnt1;
   for (int level = 0; level < 2 && tie_cnt != need; ++level) {
-    for (int b = tid; b < kBins2; b += kTkThreads) sm.hist[b] = 0;
-    __syncthreads();
     const int nshift = shift - 10;
-    // The first level also gathers the OR and the AND of the bucket's keys:
-    // where their last 10 bits agree over the whole bucket, the keys left
-    // after this level are all equal and the second level is not needed.
-    uint32_t lo = 0u, la = 0xFFFFFFFFu;
-    if (in_lds) {
-      for (int c = tid; c < n_cand; c += kTkThreads) {
-        const uint32_t key = sm.cand[c][0];
-        if ((key >> shift) == prefix) {
-          atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
-          lo |= key;
-          la &= key;
-        }
-      }
-    } else {
-      for (int base = 0; base < n; base += kSlice) {
-        const f32x4 v = load4<ALIGNED>(row, base, n);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = score_key(v[e]);
-          if (base + 4 * tid + e < n && (key >> shift) == prefix) {
+    const bool built = level == 0 && level0_built;
+    if (!built) {
+      for (int b = tid; b < kBins2; b += kTkThreads) sm.hist[b] = 0;
+      __syncthreads();
+      // The first level also gathers the OR and the AND of the bucket's keys:
+      // where their last 10 bits agree over the whole bucket, the keys left
+      // after this level are all equal and the second level is not needed.
+      uint32_t lo = 0u, la = 0xFFFFFFFFu;
+      if (in_lds) {
+        for (int c = tid; c < n_cand; c += kTkThreads) {
+          const uint32_t key = sm.cand[c][0];
+          if ((key >> shift) == prefix) {
             atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
             lo |= key;
             la &= key;
           }
         }
+      } else {
+        for (int base = 0; base < n; base += kSlice) {
+          const f32x4 v = load4<ALIGNED>(row, base, n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = score_key(v[e]);
+            if (base + 4 * tid + e < n && (key >> shift) == prefix) {
+              atomicAdd(&sm.hist[(key >> nshift) & 1023u], 1u);
+              lo |= key;
+              la &= key;
+            }
+          }
+        }
       }
+      if (level == 0) publish_low_bits(sm, lo, la);
+      __syncthreads();
     }
-    if (level == 0) publish_low_bits(sm, lo, la);
-    __syncthreads();
     uint32_t b, above, cnt;
-    select_bucket(sm, kBins2, need, &b, &above, &cnt, buf);
+    select_bucket(built ? sm.hist2 : sm.hist, sm, kBins2, need, &b, &above, &cnt, buf);
     need -= above;
     prefix = (prefix << 10) | b;
     shift = nshift;
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
   uint32_t bs = 0;
   if (spec) {
     uint32_t a_s, c_s;
-    select_bucket(sm, kBins1, need_s, &bs, &a_s, &c_s, buf);
+    select_bucket(sm.hist, sm, kBins1, need_s, &bs, &a_s, &c_s, buf);
   }
 
   // ---- one pass: the histogram of groups 1.. and, when speculating, the
@@ -397,7 +404,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
   }
   __syncthreads();
   uint32_t b1, above1, cnt1;
-  select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
+  select_bucket(sm.hist, sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
   const bool spec_ok = spec && b1 >= bs && cbase <= static_cast<uint32_t>(kTkCap);
   const bool in_lds = spec_ok || above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
   int n_cand = static_cast<int>(spec_ok ? cbase : above1 + cnt1);
@@ -446,7 +453,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
     }
   }
   __syncthreads();
-  select_tail<ALIGNED>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds, n_cand);
+  select_tail<ALIGNED>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds, n_cand, false);
 }
 
 // Rows of at most NV * 2048 keys: the row is read once, into registers
@@ -476,6 +483,7 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
     v[s] = load4<true>(row, s * kSlice, n);
   }
   for (int b = 4 * tid; b < kBins1; b += 4 * kTkThreads) *reinterpret_cast<u32x4*>(&sm.hist[b]) = u32x4{0u, 0u, 0u, 0u};
+  for (int b = 4 * tid; b < kBins2; b += 4 * kTkThreads) *reinterpret_cast<u32x4*>(&sm.hist2[b]) = u32x4{0u, 0u, 0u, 0u};
   if (tid == 0) {
     sm.low_or = 0u;
     sm.low_and = 0xFFFFFu;
@@ -491,10 +499,12 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
   }
   lds_sync();
   uint32_t b1, above1, cnt1;
-  select_bucket(sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
+  select_bucket(sm.hist, sm, kBins1, static_cast<uint32_t>(k), &b1, &above1, &cnt1, buf);
   const bool in_lds = above1 + cnt1 <= static_cast<uint32_t>(kTkCap);
   if (in_lds) {
-    uint32_t cbase = 0;
+    // The compaction also builds the first refinement level: the histogram of
+    // the next 10 bits over bucket b1's keys, and their OR / AND.
+    uint32_t cbase = 0, lo = 0u, la = 0xFFFFFFFFu;
 #pragma unroll
     for (int s0 = 0; s0 < NV; s0 += 4) {
       uint64_t packed = 0;  // 4 x 16-bit per-slice counts (each slice total <= 2048)
@@ -517,15 +527,21 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
           if (j < n && (key[s][e] >> 20) >= b1) {
             sm.cand[pos] = u32x2{key[s][e], static_cast<uint32_t>(j)};
             ++pos;
+            if ((key[s][e] >> 20) == b1) {
+              atomicAdd(&sm.hist2[(key[s][e] >> 10) & 1023u], 1u);
+              lo |= key[s][e];
+              la &= key[s][e];
+            }
           }
         }
         slice_base += static_cast<uint32_t>((tot >> (16 * (s - s0))) & 0xFFFF);
       }
       cbase = slice_base;
     }
+    publish_low_bits(sm, lo, la);
     __syncthreads();
   }
-  select_tail<true>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds, static_cast<int>(above1 + cnt1));
+  select_tail<true>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds, static_cast<int>(above1 + cnt1), in_lds);
 }
 
 }  // namespace
