@@ -237,35 +237,45 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
   // ---- emit in index order.
   uint32_t gt_base = 0, tie_base = 0;
   if (in_lds) {
-    for (int base = 0; base < n_cand; base += kSlice) {
-      uint32_t gt[4], tie[4];
-      int32_t jj[4];
+    // Two slices per block scan: each 32-bit half of the scanned value packs
+    // the two slices' counts in 16-bit fields (a slice holds <= 2048 keys).
+    for (int base = 0; base < n_cand; base += 2 * kSlice) {
+      uint32_t gt[2][4], tie[2][4];
+      int32_t jj[2][4];
       uint32_t cgt = 0, ctie = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = base + 4 * tid + e;
-        const bool valid = c < n_cand;
-        const u32x2 kv = valid ? sm.cand[c] : u32x2{0u, 0xFFFFFFFFu};
-        const uint32_t key = kv[0];
-        jj[e] = static_cast<int32_t>(kv[1]);
-        gt[e] = valid && (key >> shift) > prefix;
-        tie[e] = valid && (key >> shift) == prefix;
-        cgt += gt[e];
-        ctie += tie[e];
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = base + h * kSlice + 4 * tid + e;
+          const bool valid = c < n_cand;
+          const u32x2 kv = valid ? sm.cand[c] : u32x2{0u, 0xFFFFFFFFu};
+          const uint32_t key = kv[0];
+          jj[h][e] = static_cast<int32_t>(kv[1]);
+          gt[h][e] = valid && (key >> shift) > prefix;
+          tie[h][e] = valid && (key >> shift) == prefix;
+          cgt += gt[h][e] << (16 * h);
+          ctie += tie[h][e] << (16 * h);
+        }
       }
       uint64_t tot;
       const uint64_t excl = block_excl_scan((static_cast<uint64_t>(ctie) << 32) | cgt, &tot, sm, buf);
-      uint32_t g = gt_base + static_cast<uint32_t>(excl);
-      uint32_t t = tie_base + static_cast<uint32_t>(excl >> 32);
+      const uint32_t egt = static_cast<uint32_t>(excl), etie = static_cast<uint32_t>(excl >> 32);
+      const uint32_t tgt = static_cast<uint32_t>(tot), ttie = static_cast<uint32_t>(tot >> 32);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pos = gt[e] ? g + min(t, r) : g + t;  // < k by construction
-        if ((gt[e] || (tie[e] && t < r)) && pos < static_cast<uint32_t>(k)) out[pos] = jj[e];
-        g += gt[e];
-        t += tie[e];
+      for (int h = 0; h < 2; ++h) {
+        uint32_t g = gt_base + (h ? (tgt & 0xFFFFu) + (egt >> 16) : (egt & 0xFFFFu));
+        uint32_t t = tie_base + (h ? (ttie & 0xFFFFu) + (etie >> 16) : (etie & 0xFFFFu));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t pos = gt[h][e] ? g + min(t, r) : g + t;  // < k by construction
+          if ((gt[h][e] || (tie[h][e] && t < r)) && pos < static_cast<uint32_t>(k)) out[pos] = jj[h][e];
+          g += gt[h][e];
+          t += tie[h][e];
+        }
       }
-      gt_base += static_cast<uint32_t>(tot);
-      tie_base += static_cast<uint32_t>(tot >> 32);
+      gt_base += (tgt & 0xFFFFu) + (tgt >> 16);
+      tie_base += (ttie & 0xFFFFu) + (ttie >> 16);
     }
   } else {
     for (int base = 0; base < n; base += kSlice) {
