@@ -25,6 +25,7 @@ EXPORTED = (
     "dsa_prefill_chunk",
     "dsa_sparse_mla_decode_workspace_bytes",
     "dsa_sparse_mla_decode",
+    "dsa_self_test",
     "dsa_status_string",
     "dsa_version",
 )
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk,
                   L.dsa_sparse_mla_decode):
             f.restype = ctypes.c_int
+        L.dsa_self_test.argtypes = []
+        L.dsa_self_test.restype = ctypes.c_int
         L.dsa_status_string.argtypes = [ctypes.c_int]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_int32
@@ -96,6 +99,11 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return int(lib().dsa_version())
+
+
+def self_test() -> None:
+    """Runs the matrix-core layout self-test on the current device (raises on failure)."""
+    _check("dsa_self_test", lib().dsa_self_test())
 
 
 def make_dims(cfg, n_q: Optional[int] = None, offset: Optional[int] = None) -> Dims:
@@ -128,8 +136,58 @@ def _contig(*ts):
             raise ValueError("tensors passed to the DSA library must be contiguous")
 
 
+def _fits(t, elems: int, itemsize: int, name: str) -> None:
+    """Raises ValueError unless tensor ``t`` holds ``elems`` elements of ``itemsize`` bytes.
+
+    A host-side guard only: a tensor smaller than what the dims describe would
+    make a kernel write or read past its allocation.
+    """
+    if t is None:
+        return
+    if t.element_size() != itemsize:
+        raise ValueError(f"{name}: element size {t.element_size()} B, the dims need {itemsize} B")
+    if t.numel() < elems:
+        raise ValueError(f"{name}: {t.numel()} elements, the dims need at least {elems}")
+
+
+def _act_size(dims: Dims) -> int:
+    return 2 if dims.act_dtype == DSA_BF16 else 4
+
+
+def _idx_size(dims: Dims) -> int:
+    return 2 if dims.idx_dtype == DSA_BF16 else 4
+
+
+def _check_indexer_sizes(dims: Dims, q_idx, w_idx, k_idx, scores, ld: int) -> None:
+    if dims.n_q <= 0:
+        return
+    _fits(q_idx, dims.n_q * dims.n_idx_heads * dims.d_idx, _idx_size(dims), "q_idx")
+    _fits(w_idx, dims.n_q * dims.n_idx_heads, 4, "w_idx")
+    _fits(k_idx, (dims.offset + dims.n_q) * dims.d_idx, _idx_size(dims), "k_idx_cache")
+    _fits(scores, dims.n_q * int(ld), 4, "scores")
+
+
+def _check_topk_sizes(dims: Dims, scores, ld: int, idx) -> None:
+    if dims.n_q <= 0:
+        return
+    _fits(scores, dims.n_q * int(ld), 4, "scores")
+    _fits(idx, dims.n_q * dims.top_k, 4, "idx")
+
+
+def _check_mla_sizes(dims: Dims, q, kv, idx, out, lse) -> None:
+    if dims.n_q <= 0:
+        return
+    d_qk = dims.d_latent + dims.d_rope
+    _fits(q, dims.n_q * dims.n_heads * d_qk, _act_size(dims), "q")
+    _fits(kv, (dims.offset + dims.n_q) * d_qk, _act_size(dims), "kv_cache")
+    _fits(idx, dims.n_q * dims.top_k, 4, "idx")
+    _fits(out, dims.n_q * dims.n_heads * dims.d_latent, 4, "out")
+    _fits(lse, dims.n_q * dims.n_heads, 4, "lse")
+
+
 def indexer_scores(dims: Dims, q_idx, w_idx, k_idx, scores, ld: int, stream=None) -> None:
     _contig(q_idx, w_idx, k_idx, scores)
+    _check_indexer_sizes(dims, q_idx, w_idx, k_idx, scores, ld)
     _check("dsa_indexer_scores", lib().dsa_indexer_scores(
         ctypes.byref(dims), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(scores), int(ld),
         _stream(stream)))
@@ -141,6 +199,7 @@ def topk_workspace_bytes(dims: Dims) -> int:
 
 def topk_select(dims: Dims, scores, ld: int, idx, workspace=None, stream=None) -> None:
     _contig(scores, idx)
+    _check_topk_sizes(dims, scores, ld, idx)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_topk_select", lib().dsa_topk_select(
         ctypes.byref(dims), _ptr(scores), int(ld), _ptr(idx), _ptr(workspace), ws,
@@ -149,6 +208,7 @@ def topk_select(dims: Dims, scores, ld: int, idx, workspace=None, stream=None) -
 
 def sparse_mla_fwd(dims: Dims, q, kv, idx, out, lse=None, stream=None) -> None:
     _contig(q, kv, idx, out, lse)
+    _check_mla_sizes(dims, q, kv, idx, out, lse)
     _check("dsa_sparse_mla_fwd", lib().dsa_sparse_mla_fwd(
         ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse),
         _stream(stream)))
@@ -160,6 +220,7 @@ def sparse_mla_decode_workspace_bytes(dims: Dims) -> int:
 
 def sparse_mla_decode(dims: Dims, q, kv, idx, out, lse=None, workspace=None, stream=None) -> None:
     _contig(q, kv, idx, out, lse, workspace)
+    _check_mla_sizes(dims, q, kv, idx, out, lse)
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_sparse_mla_decode", lib().dsa_sparse_mla_decode(
         ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse), _ptr(workspace), ws,
@@ -169,6 +230,12 @@ def sparse_mla_decode(dims: Dims, q, kv, idx, out, lse=None, workspace=None, str
 def prefill_chunk(dims: Dims, q, kv_chunk, q_idx, w_idx, k_idx_chunk, kv_cache, k_idx_cache, scores, ld: int,
                   idx, out, lse=None, workspace=None, stream=None) -> None:
     _contig(q, kv_chunk, q_idx, w_idx, k_idx_chunk, kv_cache, k_idx_cache, scores, idx, out, lse)
+    _check_indexer_sizes(dims, q_idx, w_idx, k_idx_cache, scores, ld)
+    _check_topk_sizes(dims, scores, ld, idx)
+    _check_mla_sizes(dims, q, kv_cache, idx, out, lse)
+    if dims.n_q > 0:
+        _fits(kv_chunk, dims.n_q * (dims.d_latent + dims.d_rope), _act_size(dims), "kv_chunk")
+        _fits(k_idx_chunk, dims.n_q * dims.d_idx, _idx_size(dims), "k_idx_chunk")
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_prefill_chunk", lib().dsa_prefill_chunk(
         ctypes.byref(dims), _ptr(q), _ptr(kv_chunk), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx_chunk),

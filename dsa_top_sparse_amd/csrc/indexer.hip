@@ -15,6 +15,7 @@
 // consecutive keys of one query per lane); the other widths store one fp32
 // score per lane, 32 lanes covering 32 consecutive keys of one query row.
 #include "common.h"
+#include "device_checks.h"
 #include "kernels.h"
 
 namespace dsa {
@@ -353,23 +354,41 @@ hipError_t launch_mfma(const IndexerArgs& a, hipStream_t s) {
   if (n_units > (int64_t)1 << 30) return hipErrorInvalidValue;
   const int units_per_xcd = (int)((n_units + 7) / 8);
   const int grid = units_per_xcd * 8;
-  if (D == 128 && kpu % kIdxStageKeys == 0) {
-    hipLaunchKernelGGL(indexer_lds_kernel, dim3(grid), dim3(kIdx8Threads), 0, s, a.n_q, a.offset,
+  if (D == 128 && kpu % kIdxStageKeys == 0)
+    return launch_kernel(indexer_lds_kernel, dim3(grid), dim3(kIdx8Threads), 0, s, a.n_q, a.offset,
+                         static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx), a.scores,
+                         a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
+  return launch_kernel(indexer_mfma_kernel<D>, dim3(grid), dim3(kIdxThreads), 0, s, a.n_q, a.offset,
                        static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx), a.scores,
                        a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
-    return hipGetLastError();
+}
+
+hipError_t check_indexer_kernels_now() {
+  const struct {
+    const void* fn;
+    int threads;
+    size_t dyn_lds;
+  } ks[] = {
+      {reinterpret_cast<const void*>(indexer_lds_kernel), kIdx8Threads, 0},
+      {reinterpret_cast<const void*>(indexer_mfma_kernel<32>), kIdxThreads, 0},
+      {reinterpret_cast<const void*>(indexer_mfma_kernel<64>), kIdxThreads, 0},
+      {reinterpret_cast<const void*>(indexer_mfma_kernel<128>), kIdxThreads, 0},
+      {reinterpret_cast<const void*>(indexer_mfma_kernel<256>), kIdxThreads, 0},
+      {reinterpret_cast<const void*>(indexer_plain_kernel<uint16_t>), 256, sizeof(float) * kPlainIndexerMaxElems},
+      {reinterpret_cast<const void*>(indexer_plain_kernel<float>), 256, sizeof(float) * kPlainIndexerMaxElems},
+  };
+  for (const auto& k : ks) {
+    const hipError_t e = check_launch_limits(k.fn, k.threads, k.dyn_lds);
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(indexer_mfma_kernel<D>, dim3(grid), dim3(kIdxThreads), 0, s, a.n_q, a.offset,
-                     static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx),
-                     a.scores, a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace
 
-bool indexer_fast_path(const IndexerArgs& a) {
-  return a.bf16 && a.n_idx_heads == kIdxHeads &&
-         (a.d_idx == 32 || a.d_idx == 64 || a.d_idx == 128 || a.d_idx == 256);
+hipError_t check_indexer_kernels() {
+  static PerDeviceCache cache;
+  return once_per_device(cache, check_indexer_kernels_now);
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
@@ -386,14 +405,12 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   const size_t lds = sizeof(float) * (size_t)a.n_idx_heads * a.d_idx;
   if (a.bf16)
-    hipLaunchKernelGGL(indexer_plain_kernel<uint16_t>, dim3((unsigned)gx, a.n_q), dim3(256), lds, s, a.n_q,
-                       a.offset, a.n_idx_heads, a.d_idx, static_cast<const uint16_t*>(a.q_idx), a.w,
-                       static_cast<const uint16_t*>(a.k_idx), a.scores, a.ld);
-  else
-    hipLaunchKernelGGL(indexer_plain_kernel<float>, dim3((unsigned)gx, a.n_q), dim3(256), lds, s, a.n_q,
-                       a.offset, a.n_idx_heads, a.d_idx, static_cast<const float*>(a.q_idx), a.w,
+    return launch_kernel(indexer_plain_kernel<uint16_t>, dim3((unsigned)gx, a.n_q), dim3(256), lds, s, a.n_q,
+                         a.offset, a.n_idx_heads, a.d_idx, static_cast<const uint16_t*>(a.q_idx), a.w,
+                         static_cast<const uint16_t*>(a.k_idx), a.scores, a.ld);
+  return launch_kernel(indexer_plain_kernel<float>, dim3((unsigned)gx, a.n_q), dim3(256), lds, s, a.n_q, a.offset,
+                       a.n_idx_heads, a.d_idx, static_cast<const float*>(a.q_idx), a.w,
                        static_cast<const float*>(a.k_idx), a.scores, a.ld);
-  return hipGetLastError();
 }
 
 }  // namespace dsa

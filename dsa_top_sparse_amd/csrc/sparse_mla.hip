@@ -29,6 +29,7 @@
 // The two roles run side by side on every SIMD, one tile apart, and meet at
 // one barrier per tile (details at the kernel).
 #include "common.h"
+#include "device_checks.h"
 #include "kernels.h"
 
 #include <type_traits>
@@ -133,6 +134,7 @@ constexpr int kDL = 512;            // latent / value dims
 constexpr int kDR = 64;             // rope dims
 constexpr int kDQK = kDL + kDR;     // 576
 constexpr int kTile = 32;           // selected slots per tile
+static_assert(kTile == kDecodeTile, "decode splits are whole tiles");
 constexpr int kThreads = 512;       // 8 waves: 4 score waves + 4 P V waves
 constexpr int kStages = 4;          // LDS tile stages (hi/lo queries use 3; P's lo part takes the 4th)
 constexpr int kRowBytes = kDQK * 2;              // 1152 = 72 pieces of 16 bytes
@@ -781,27 +783,31 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(int n_q, i
   if (lse && threadIdx.x == 0) lse[(int64_t)i * kH + h] = sum > 0.0f ? m + logf(sum) : -INFINITY;
 }
 
-}  // namespace
-
-MlaSplit mla_decode_split(const MlaArgs& a) {
-  MlaSplit sp{1, a.top_k};
-  if (!mla_fast_path(a) || a.n_q <= 0) return sp;
-  // enough workgroups to occupy the chip (one per CU), splits of whole tiles
-  const int want = (kDecodeTargetGroups + a.n_q - 1) / a.n_q;
-  const int max_splits = (a.top_k + kDecodeMinSlots - 1) / kDecodeMinSlots;
-  const int splits = want < max_splits ? want : max_splits;
-  if (splits <= 1) return sp;
-  int slots = (a.top_k + splits - 1) / splits;
-  slots = (slots + kTile - 1) / kTile * kTile;
-  sp.splits = (a.top_k + slots - 1) / slots;
-  sp.split_slots = slots;
-  return sp;
+hipError_t check_mla_kernels_now() {
+  const struct {
+    const void* fn;
+    int threads;
+    size_t dyn_lds;
+  } ks[] = {
+      {reinterpret_cast<const void*>(mla_mfma_kernel), kThreads, 0},
+      {reinterpret_cast<const void*>(mla_combine_kernel), kCombineThreads, 0},
+      {reinterpret_cast<const void*>(mla_plain_kernel<uint16_t>), kPlainThreads,
+       sizeof(float) * kPlainMlaMaxDqk + (sizeof(float) + sizeof(int32_t)) * kPlainMlaMaxTopk},
+      {reinterpret_cast<const void*>(mla_plain_kernel<float>), kPlainThreads,
+       sizeof(float) * kPlainMlaMaxDqk + (sizeof(float) + sizeof(int32_t)) * kPlainMlaMaxTopk},
+  };
+  for (const auto& k : ks) {
+    const hipError_t e = check_launch_limits(k.fn, k.threads, k.dyn_lds);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-size_t mla_decode_workspace_bytes(const MlaArgs& a) {
-  const MlaSplit sp = mla_decode_split(a);
-  if (sp.splits <= 1) return 0;
-  return (size_t)sp.splits * a.n_q * kH * (kDL + 1) * sizeof(float);
+}  // namespace
+
+hipError_t check_mla_kernels() {
+  static PerDeviceCache cache;
+  return once_per_device(cache, check_mla_kernels_now);
 }
 
 hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t s) {
@@ -811,41 +817,31 @@ hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t s) {
   float* part_out = static_cast<float*>(workspace);
   float* part_lse = part_out + (size_t)sp.splits * a.n_q * kH * kDL;
   const float scale_log2 = a.sm_scale * 1.44269504088896340736f;
-  hipLaunchKernelGGL(mla_mfma_kernel, dim3(a.n_q, sp.splits), dim3(kThreads), 0, s, a.n_q, a.offset, a.top_k,
-                     sp.split_slots, scale_log2, static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.kv), a.idx, part_out, part_lse);
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(a.n_q, kH), dim3(kCombineThreads), 0, s, a.n_q, sp.splits, part_out,
-                     part_lse, a.out, a.lse);
-  return hipGetLastError();
-}
-
-bool mla_fast_path(const MlaArgs& a) {
-  // top_k % 4 == 0: the index ring is filled with 16-byte loads from 16-byte aligned rows.
-  // The cache must stay below 4 GiB (32-bit byte offsets).
-  return a.bf16 && a.n_heads == kH && a.d_latent == kDL && a.d_rope == kDR && a.top_k % 4 == 0 &&
-         (int64_t)(a.offset + a.n_q) * kRowBytes < ((int64_t)1 << 32);
+  hipError_t e = launch_kernel(mla_mfma_kernel, dim3(a.n_q, sp.splits), dim3(kThreads), 0, s, a.n_q, a.offset,
+                               a.top_k, sp.split_slots, scale_log2, static_cast<const uint16_t*>(a.q),
+                               static_cast<const uint16_t*>(a.kv), a.idx, part_out, part_lse);
+  if (e != hipSuccess) return e;
+  return launch_kernel(mla_combine_kernel, dim3(a.n_q, kH), dim3(kCombineThreads), 0, s, a.n_q, sp.splits,
+                       static_cast<const float*>(part_out), static_cast<const float*>(part_lse), a.out, a.lse);
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   if (mla_fast_path(a)) {
     const float scale_log2 = a.sm_scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL(mla_mfma_kernel, dim3(a.n_q, 1), dim3(kThreads), 0, s, a.n_q, a.offset, a.top_k, a.top_k,
-                       scale_log2, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv), a.idx,
-                       a.out, a.lse);
-    return hipGetLastError();
+    return launch_kernel(mla_mfma_kernel, dim3(a.n_q, 1), dim3(kThreads), 0, s, a.n_q, a.offset, a.top_k, a.top_k,
+                         scale_log2, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv), a.idx,
+                         a.out, a.lse);
   }
   const int d_qk = a.d_latent + a.d_rope;
   const size_t lds = sizeof(float) * (size_t)d_qk + (sizeof(float) + sizeof(int32_t)) * (size_t)a.top_k;
   if (a.bf16)
-    hipLaunchKernelGGL(mla_plain_kernel<uint16_t>, dim3(a.n_q, a.n_heads), dim3(kPlainThreads), lds, s, a.offset,
-                       a.n_heads, d_qk, a.d_latent, a.top_k, a.sm_scale, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.kv), a.idx, a.out, a.lse);
-  else
-    hipLaunchKernelGGL(mla_plain_kernel<float>, dim3(a.n_q, a.n_heads), dim3(kPlainThreads), lds, s, a.offset,
+    return launch_kernel(mla_plain_kernel<uint16_t>, dim3(a.n_q, a.n_heads), dim3(kPlainThreads), lds, s, a.offset,
+                         a.n_heads, d_qk, a.d_latent, a.top_k, a.sm_scale, static_cast<const uint16_t*>(a.q),
+                         static_cast<const uint16_t*>(a.kv), a.idx, a.out, a.lse);
+  return launch_kernel(mla_plain_kernel<float>, dim3(a.n_q, a.n_heads), dim3(kPlainThreads), lds, s, a.offset,
                        a.n_heads, d_qk, a.d_latent, a.top_k, a.sm_scale, static_cast<const float*>(a.q),
                        static_cast<const float*>(a.kv), a.idx, a.out, a.lse);
-  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -35,6 +35,7 @@
 // instead (same arithmetic).
 // Block scans run their wave part on DPP row shifts and broadcasts.
 #include "common.h"
+#include "device_checks.h"
 #include "kernels.h"
 
 namespace dsa {
@@ -554,25 +555,34 @@ __global__ __launch_bounds__(kTkThreads) __attribute__((amdgpu_waves_per_eu(4)))
   select_tail<true>(sm, buf, row, n, k, out, b1, above1, cnt1, in_lds, static_cast<int>(above1 + cnt1), in_lds);
 }
 
+hipError_t check_topk_kernels_now() {
+  const void* ks[] = {reinterpret_cast<const void*>(topk_reg_kernel<8>), reinterpret_cast<const void*>(topk_reg_kernel<9>),
+                      reinterpret_cast<const void*>(topk_kernel<true>), reinterpret_cast<const void*>(topk_kernel<false>)};
+  for (const void* k : ks) {
+    const hipError_t e = check_launch_limits(k, kTkThreads, 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t check_topk_kernels() {
+  static PerDeviceCache cache;
+  return once_per_device(cache, check_topk_kernels_now);
+}
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   const bool aligned = (a.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
   const int64_t n_max = (int64_t)a.offset + a.n_q;  // longest causal row
+  const dim3 grid(a.n_q), block(kTkThreads);
   if (aligned && n_max <= 8 * kSlice)
-    hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores, a.ld,
-                       a.idx);
-  else if (aligned && n_max <= 9 * kSlice)
-    hipLaunchKernelGGL(topk_reg_kernel<9>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores, a.ld,
-                       a.idx);
-  else if (aligned)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores,
-                       a.ld, a.idx);
-  else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(a.n_q), dim3(kTkThreads), 0, s, a.offset, a.top_k, a.scores,
-                       a.ld, a.idx);
-  return hipGetLastError();
+    return launch_kernel(topk_reg_kernel<8>, grid, block, 0, s, a.offset, a.top_k, a.scores, a.ld, a.idx);
+  if (aligned && n_max <= 9 * kSlice)
+    return launch_kernel(topk_reg_kernel<9>, grid, block, 0, s, a.offset, a.top_k, a.scores, a.ld, a.idx);
+  if (aligned) return launch_kernel(topk_kernel<true>, grid, block, 0, s, a.offset, a.top_k, a.scores, a.ld, a.idx);
+  return launch_kernel(topk_kernel<false>, grid, block, 0, s, a.offset, a.top_k, a.scores, a.ld, a.idx);
 }
 
 }  // namespace dsa

@@ -34,6 +34,9 @@
  *    enqueued asynchronously on it; a call returns before the GPU finishes.
  *  - Errors: invalid arguments return a negative status BEFORE anything is
  *    enqueued; a failed launch returns DSA_ERR_DEVICE. Nothing aborts.
+ *  - Before the first launch on a device each call checks its kernels'
+ *    launch limits (block size, LDS, registers) against the device
+ *    (DSA_ERR_UNSUPPORTED if one does not fit) and runs dsa_self_test.
  *  - Inputs are only read and outputs are only written; outputs must not alias
  *    inputs.
  */
@@ -198,6 +201,25 @@ DSA_API dsa_status dsa_prefill_chunk(const dsa_dims *dims, const void *q, const 
                                      void *kv_cache, void *k_idx_cache, float *scores, int64_t ld,
                                      int32_t *idx, float *out, float *lse, void *workspace,
                                      size_t ws_bytes, void *stream);
+
+/*
+ * dsa_self_test -- the matrix-core layout self-test on the current device.
+ *
+ * Runs known small-integer products through each matrix-core instruction form
+ * and operand path the fast kernels use (register operands of the 16x16x32
+ * and 32x32x16 bf16 forms, and the transposing LDS read that feeds the value
+ * operand of attention) and compares every result with the exact product
+ * computed on the host. A layout other than the one the kernels assume (for
+ * example a transposed operand) fails it. Prompted by TensorFold issue #743,
+ * "Proposal: restore single-Mac GLM-5.3-Flash on the M3 Ultra", which asks
+ * for a load-time fragment-layout check that catches a transposed operand.
+ *
+ * Synchronous; runs once per device (later calls return the cached result).
+ * Every other call runs it before its first launch on a device, unless its
+ * stream is being captured into a graph: call this function before capturing.
+ * Returns DSA_OK, or DSA_ERR_DEVICE when a product is wrong or HIP fails.
+ */
+DSA_API dsa_status dsa_self_test(void);
 
 /* Static description of a status code (never NULL). */
 DSA_API const char *dsa_status_string(dsa_status status);

@@ -2,12 +2,15 @@
 
 Every case calls the library through its C ABI (``dsa_top_sparse_amd.binding``)
 on seeded synthetic inputs and compares with ``oracle``:
-  * indexer scores and top-k indices: bit-exact on sampled query rows (all
-    rows for the small configs), plus the selection properties on every row;
-  * attention: max |out - ref| <= 4e-3, relative L2 <= 5e-3, |lse - ref| <= 1e-3
-    on the sampled rows (the fp64 oracle is too slow for every row at 8k x 2k).
+  * the five workloads C0-C4 on EVERY query row, in blocks of rows: indexer
+    scores and top-k indices bit-exact, attention within max |out - ref| <=
+    4e-3, relative L2 <= 5e-3 (per block, hence over the whole tensor too) and
+    |lse - ref| <= 1e-3; the top-k properties also on every row against the
+    GPU's scores;
+  * edge cases (ragged sizes, other shapes, long rows, ties, padding, restart,
+    decode splits, chunked prefill) on all rows of smaller inputs.
 """
-import sys
+import math
 
 import numpy as np
 import pytest
@@ -15,17 +18,11 @@ import pytest
 import golden_cases
 import oracle
 from dsa_top_sparse_amd import binding, synth
+from parity_checks import ATOL, LSE_ATOL, attention_errors, check_attention, check_topk_properties, say
 
 pytestmark = pytest.mark.gpu
 
-ATOL = 4e-3
-RTOL_L2 = 5e-3
-LSE_ATOL = 1e-3
-
-
-def _say(msg):
-    print(f"[gpu-case] {msg}", flush=True)
-    sys.stdout.flush()
+_say = say
 
 
 @pytest.fixture(scope="module")
@@ -38,14 +35,6 @@ def torch_cuda():
     return torch
 
 
-def sample_rows(n_q, seed, extra=24):
-    fixed = [0, 1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 511, 512, 513, 1000, n_q // 2,
-             n_q - 2, n_q - 1]
-    rng = np.random.default_rng(1000 + seed)
-    rnd = rng.choice(n_q, size=min(extra, n_q), replace=False).tolist()
-    return sorted({r for r in fixed + rnd if 0 <= r < n_q})
-
-
 def run_gpu(torch, cfg, inputs, ld=None, with_lse=True):
     dev = binding.to_device(inputs)
     outs = binding.alloc_outputs(cfg, ld=ld, with_lse=with_lse)
@@ -54,86 +43,59 @@ def run_gpu(torch, cfg, inputs, ld=None, with_lse=True):
     return dev, outs
 
 
-def check_attention(got_out, got_lse, ref_out, ref_lse, label):
-    diff = np.abs(got_out.astype(np.float64) - ref_out)
-    max_abs = float(diff.max()) if diff.size else 0.0
-    rel = float(np.linalg.norm(got_out.astype(np.float64) - ref_out) / max(np.linalg.norm(ref_out), 1e-300))
-    _say(f"{label}: attention max_abs={max_abs:.3e} rel_l2={rel:.3e}")
-    assert max_abs <= ATOL, f"{label}: max abs err {max_abs}"
-    assert rel <= RTOL_L2, f"{label}: rel L2 {rel}"
-    if got_lse is not None:
-        fin = np.isfinite(ref_lse)
-        assert np.array_equal(np.isfinite(got_lse), fin)
-        if fin.any():
-            lerr = float(np.abs(got_lse[fin] - ref_lse[fin]).max())
-            assert lerr <= LSE_ATOL, f"{label}: lse err {lerr}"
+# --------------------------------------------------------- every query row
+
+ROW_BLOCK = 1024  # oracle rows per test: seconds of host time each
+WORKLOADS = ["C0", "C1", "C2", "C3", "C4"]
+BLOCKS = [(name, b) for name in WORKLOADS
+          for b in range(math.ceil(synth.CONFIGS[name].n_q / ROW_BLOCK))]
+
+_results = {}  # one workload's GPU results at a time (host copies)
 
 
-def check_topk_properties(torch, scores, idx, offset, k, label):
-    """Selection properties on every row, using the GPU's own (verified) scores."""
-    n_q = idx.shape[0]
-    pos = torch.arange(n_q, device=idx.device, dtype=torch.int64) + offset
-    n = pos + 1
-    valid = idx >= 0
-    cnt = valid.sum(1)
-    assert torch.equal(cnt, torch.clamp(n, max=k)), f"{label}: wrong selected count"
-    # ascending, in range, no duplicates
-    sel = torch.where(valid, idx.long(), torch.full_like(idx.long(), -1))
-    d = sel[:, 1:] - sel[:, :-1]
-    both = valid[:, 1:] & valid[:, :-1]
-    assert bool(((d > 0) | ~both).all()), f"{label}: not strictly ascending"
-    assert bool((sel.max(1).values <= pos).all()), f"{label}: non-causal index"
-    # valid slots form a prefix (padding at the tail only)
-    assert bool((valid[:, 1:] <= valid[:, :-1]).all())
-    rows = torch.nonzero(n > k).flatten()
-    if rows.numel() == 0:
-        return
-    chunk = 256
-    for r0 in range(0, rows.numel(), chunk):
-        rr = rows[r0:r0 + chunk]
-        S = scores[rr]  # [R][ld]
-        sel_idx = idx[rr].long()
-        sel_s = torch.gather(S, 1, sel_idx)
-        thr = sel_s.min(1).values  # k-th largest
-        col = torch.arange(S.shape[1], device=S.device)
-        causal = col[None, :] <= pos[rr][:, None]
-        greater = ((S > thr[:, None]) & causal).sum(1)
-        assert bool((greater <= k).all()), f"{label}: a larger score was left out"
-        # ties at the threshold: the kept ones are the lowest indices
-        eq = (S == thr[:, None]) & causal
-        n_eq_kept = (sel_s == thr[:, None]).sum(1)
-        rank = torch.cumsum(eq.int(), 1)  # 1-based rank among ties
-        mark = torch.zeros_like(S, dtype=torch.bool)
-        mark.scatter_(1, sel_idx, True)
-        kept_tie = eq & mark
-        assert bool(((rank <= n_eq_kept[:, None]) == kept_tie)[eq].all()), f"{label}: tie rule violated"
+def gpu_results(torch, name):
+    """Runs the whole path once per workload; returns (cfg, inputs, host outputs, error sums)."""
+    if name not in _results:
+        _results.clear()
+        cfg = synth.CONFIGS[name]
+        say(f"{name}: generate {cfg}")
+        inputs = synth.generate(cfg)
+        say(f"{name}: run GPU path")
+        dev, outs = run_gpu(torch, cfg, inputs)
+        say(f"{name}: top-k properties on every row")
+        check_topk_properties(torch, outs["scores"], outs["idx"], cfg.offset, cfg.top_k, name)
+        host = {k: outs[k].cpu().numpy() for k in ("scores", "idx", "out", "lse")}
+        del dev, outs
+        torch.cuda.empty_cache()
+        _results[name] = (cfg, inputs, host, {"se": 0.0, "sr": 0.0, "max_abs": 0.0, "blocks": 0})
+    return _results[name]
 
 
-@pytest.mark.parametrize("name", ["C0", "C1", "C2", "C3", "C4"])
-def test_config_parity(torch_cuda, name):
-    torch = torch_cuda
-    cfg = synth.CONFIGS[name]
-    _say(f"{name}: generate {cfg}")
-    inputs = synth.generate(cfg)
-    _say(f"{name}: run GPU path")
-    dev, outs = run_gpu(torch, cfg, inputs)
-    scores = outs["scores"]
-    idx = outs["idx"]
-    rows = list(range(cfg.n_q)) if name == "C0" else sample_rows(cfg.n_q, cfg.seed)
-    _say(f"{name}: oracle on {len(rows)} rows")
+@pytest.mark.parametrize("name,block", BLOCKS, ids=[f"{n}-rows{b * ROW_BLOCK}" for n, b in BLOCKS])
+def test_config_parity(torch_cuda, name, block):
+    # Rows [block * 1024, +1024) of the workload against the oracle: scores and
+    # indices bit-exact, attention and lse within tolerance.
+    cfg, inputs, host, acc = gpu_results(torch_cuda, name)
+    r0, r1 = block * ROW_BLOCK, min(cfg.n_q, (block + 1) * ROW_BLOCK)
+    rows = list(range(r0, r1))
+    say(f"{name}: oracle on rows {r0}..{r1 - 1}")
     ref = oracle.full_path(cfg, inputs, rows=rows)
-    g_scores = scores[rows].cpu().numpy()
-    assert np.array_equal(g_scores.view(np.uint32), ref["scores"].view(np.uint32)), f"{name}: scores differ"
-    g_idx = idx[rows].cpu().numpy()
-    assert np.array_equal(g_idx, ref["idx"]), f"{name}: indices differ"
-    check_attention(outs["out"][rows].cpu().numpy(), outs["lse"][rows].cpu().numpy(), ref["out"],
-                    ref["lse"], name)
-    _say(f"{name}: top-k properties on all rows")
-    check_topk_properties(torch, scores, idx, cfg.offset, cfg.top_k, name)
-    if name in ("C1", "C2"):
-        # whole score matrix against the oracle (bit-exact); cheap enough at 2k queries
-        all_ref = oracle.indexer_scores(cfg.n_q, cfg.offset, inputs["qidx"], inputs["w"], inputs["kidx"])
-        assert np.array_equal(scores.cpu().numpy().view(np.uint32), all_ref.view(np.uint32))
+    g_scores = host["scores"][r0:r1]
+    bad = np.flatnonzero(np.any(g_scores.view(np.uint32) != ref["scores"].view(np.uint32), axis=1))
+    assert bad.size == 0, f"{name}: scores differ on rows {(bad[:8] + r0).tolist()}"
+    g_idx = host["idx"][r0:r1]
+    bad = np.flatnonzero(np.any(g_idx != ref["idx"], axis=1))
+    assert bad.size == 0, f"{name}: indices differ on rows {(bad[:8] + r0).tolist()}"
+    check_attention(host["out"][r0:r1], host["lse"][r0:r1], ref["out"], ref["lse"], f"{name} rows {r0}..{r1 - 1}",
+                    row_ids=rows)
+    max_abs, _, se, sr, _ = attention_errors(host["out"][r0:r1], ref["out"])
+    acc["se"] += se
+    acc["sr"] += sr
+    acc["max_abs"] = max(acc["max_abs"], max_abs)
+    acc["blocks"] += 1
+    if acc["blocks"] * ROW_BLOCK >= cfg.n_q:
+        say(f"{name}: all {cfg.n_q} rows: attention max_abs={acc['max_abs']:.3e} "
+            f"rel_l2={math.sqrt(acc['se'] / acc['sr']):.3e}")
 
 
 @pytest.mark.parametrize("ld_pad", [3, 0])
@@ -472,6 +434,47 @@ def test_chunked_prefill_replay(torch_cuda):
     assert np.array_equal(whole["idx"][rows].cpu().numpy(), ref["idx"])
     check_attention(whole["out"][rows].cpu().numpy(), whole["lse"][rows].cpu().numpy(), ref["out"], ref["lse"],
                     "prefill replay")
+
+
+def test_prefill_replay_17k_prompt_2k_chunks(torch_cuda):
+    # The pages' 17.5k-token prompt (17,536 tokens) from empty caches in
+    # 2,048-token chunks (nine calls, the last of 1,152 tokens) and in
+    # 8,192-token chunks, against the whole prompt as one chunk: index sets,
+    # outputs and lse bit-identical; rows on both sides of every chunk edge
+    # against the oracle.
+    from dsa_top_sparse_amd import prefill
+    torch = torch_cuda
+    cfg = synth.PROMPTS["P17K"]
+    say(f"prefill 17k: generate {cfg}")
+    inputs = synth.generate(cfg)
+    dev = binding.to_device(inputs)
+    T = cfg.n_q
+    scores = torch.empty((T, T), dtype=torch.float32, device="cuda")
+    runs = {}
+    for chunk in (T, 8192, 2048):
+        say(f"prefill 17k: chunk {chunk}")
+        o = prefill.alloc_prompt_outputs(cfg)
+        prefill.run_prefill(cfg, dev, chunk, o, scores=scores)
+        torch.cuda.synchronize()
+        runs[chunk] = {k: o[k] for k in ("idx", "out", "lse")}
+    for chunk in (8192, 2048):
+        for key in ("idx", "out", "lse"):
+            assert torch.equal(runs[chunk][key], runs[T][key]), (chunk, key)
+    edges = sorted({r for c in range(0, T, 2048) for r in (c - 1, c, c + 1) if 0 <= r < T} | {T - 1})
+    say(f"prefill 17k: oracle on {len(edges)} chunk-edge rows")
+    ref = oracle.full_path(cfg, inputs, rows=edges)
+    got = runs[2048]
+    assert np.array_equal(got["idx"][edges].cpu().numpy(), ref["idx"])
+    check_attention(got["out"][edges].cpu().numpy(), got["lse"][edges].cpu().numpy(), ref["out"], ref["lse"],
+                    "prefill 17k", row_ids=edges)
+
+
+def test_self_test_and_launch_limits(torch_cuda):
+    # The matrix-core layout self-test passes on this device (and is cached),
+    # and every entry point's launch-limit check lets the workloads' kernels run
+    # (the config parity tests above already launched them).
+    binding.self_test()
+    binding.self_test()
 
 
 @pytest.mark.parametrize("n_q", [1, 3, 4, 40])
