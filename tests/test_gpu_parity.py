@@ -212,17 +212,19 @@ def test_other_shapes_bf16(torch_cuda, shape):
     check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], f"{shape}")
 
 
+@pytest.mark.parametrize("off", [30000, 70000])
 @pytest.mark.parametrize("order", ["increasing", "decreasing", "random"])
-def test_topk_long_rows_speculation(torch_cuda, order):
-    # Rows past 16,384 keys take the streaming select, which guesses a
-    # candidate bucket from each row's first 8,192 keys. Increasing scores make
-    # the guess far too low (the candidates overflow LDS), decreasing scores
-    # make it too high (the k-th key lies below it); both must fall back to a
-    # second read. Random integer scores take the one-pass path. Ties at
-    # several places; every row against the oracle.
+def test_topk_long_rows_speculation(torch_cuda, order, off):
+    # Both select kernels guess from the start of each row: the filtered one a
+    # threshold from its first 2,048 keys, the streamed one a bucket from its
+    # first 8,192. Increasing scores make the guess far too low (the candidates
+    # overflow LDS), decreasing scores make it too high (fewer than k keys pass
+    # it); both must fall back to a second read. Random integer scores take the
+    # one-pass path. Ties at several places; 30,000-key rows (filtered kernel)
+    # and 70,000-key rows (streamed kernel); every row against the oracle.
     torch = torch_cuda
     rng = np.random.default_rng(len(order))
-    n_q, off, k = 10, 30000, 2048
+    n_q, k = 10, 2048
     ld = off + n_q
     j = np.arange(ld, dtype=np.float64)
     if order == "increasing":
@@ -235,7 +237,7 @@ def test_topk_long_rows_speculation(torch_cuda, order):
     s[:, 5000:5100] = s[0, 5000]  # a block of equal scores
     for i in range(n_q):
         s[i, off + i + 1:] = -np.inf
-    _say(f"topk long rows: {order}")
+    _say(f"topk long rows: {order} offset={off}")
     st = torch.from_numpy(s).cuda()
     idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
     cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
@@ -295,14 +297,15 @@ def test_topk_constant_low_bits(torch_cuda, off):
 
 
 @pytest.mark.parametrize("off,k,ld_pad", [(7000, 2048, 0), (17000, 2048, 0), (30000, 2048, 4), (60000, 1500, 0),
-                                          (70000, 2048, 0), (5000, 999, 1),
-                                          (16368, 2048, 0), (16369, 2048, 0), (18416, 2048, 0), (18417, 2048, 0)])
+                                          (65520, 2048, 0), (65521, 2048, 0), (70000, 2048, 0), (5000, 999, 1),
+                                          (2040, 2000, 0), (4090, 2048, 0), (16368, 2048, 0)])
 def test_topk_row_lengths(torch_cuda, off, k, ld_pad):
-    # Row lengths in both register-resident kernels (32 and 36 keys per thread:
-    # rows of up to 16,384 and 18,432 keys, each limit hit exactly and passed
-    # by one key), the streamed kernel beyond (up to 70,016 keys), and
-    # unaligned leading dimensions; integer-valued scores with many ties plus
-    # random floats, vs the oracle.
+    # Row lengths across the select kernels: the filtered kernel up to 65,536
+    # keys (that limit hit exactly and passed by one key), rows shorter than
+    # its 2,048-key threshold sample, rows around its candidate capacity, the
+    # streamed kernel beyond, and unaligned leading dimensions (streamed
+    # kernel); integer-valued scores with many ties plus random floats, vs
+    # the oracle.
     torch = torch_cuda
     rng = np.random.default_rng(off + k)
     n_q = 16
@@ -312,6 +315,33 @@ def test_topk_row_lengths(torch_cuda, off, k, ld_pad):
     for i in range(n_q):
         s[i, off + i + 1:] = -np.inf
     _say(f"topk rows: offset={off} k={k} ld={ld}")
+    st = torch.from_numpy(s).cuda()
+    idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
+    cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
+    binding.topk_select(binding.make_dims(cfg), st, ld, idx)
+    torch.cuda.synchronize()
+    ref = oracle.topk_select(n_q, off, k, s)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_topk_kth_far_above_sample_threshold(torch_cuda):
+    # The row's first 2,048 keys (the filtered select's threshold sample) are
+    # small, and k keys far larger sit later in the row: the threshold from the
+    # sample keeps a candidate set that holds the top k, but the k-th key lies
+    # far above the threshold, so the select finds its top digit from the
+    # candidates instead of the threshold-relative histogram. Ties among the
+    # large keys on some rows. Every row vs the oracle.
+    torch = torch_cuda
+    rng = np.random.default_rng(11)
+    n_q, off, k = 12, 14000, 2048
+    ld = off + n_q
+    s = rng.random((n_q, ld)).astype(np.float32)
+    s[:, 2048:] *= 0.5  # below the sample's threshold (about 0.8)
+    for i in range(n_q):
+        big = rng.choice(np.arange(2048, off), size=k + 40, replace=False)
+        s[i, big] = (1000.0 + rng.integers(0, 50 if i % 2 else 5000, size=big.size)).astype(np.float32)
+        s[i, off + i + 1:] = -np.inf
+    _say("topk k-th far above the sample threshold")
     st = torch.from_numpy(s).cuda()
     idx = torch.empty((n_q, k), dtype=torch.int32, device="cuda")
     cfg = synth.CONFIGS["C2"].replace(n_q=n_q, offset=off, top_k=k)
