@@ -25,6 +25,7 @@ EXPORTED = (
     "dsa_prefill_chunk",
     "dsa_sparse_mla_decode_workspace_bytes",
     "dsa_sparse_mla_decode",
+    "dsa_sparse_mla_decode_noalloc",
     "dsa_self_test",
     "dsa_status_string",
     "dsa_version",
@@ -81,8 +82,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_mla_decode_workspace_bytes.argtypes = [dp]
         L.dsa_sparse_mla_decode_workspace_bytes.restype = sz
         L.dsa_sparse_mla_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dsa_sparse_mla_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp]
         for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk,
-                  L.dsa_sparse_mla_decode):
+                  L.dsa_sparse_mla_decode, L.dsa_sparse_mla_decode_noalloc):
             f.restype = ctypes.c_int
         L.dsa_self_test.argtypes = []
         L.dsa_self_test.restype = ctypes.c_int
@@ -225,6 +227,13 @@ def sparse_mla_decode(dims: Dims, q, kv, idx, out, lse=None, workspace=None, str
     _check("dsa_sparse_mla_decode", lib().dsa_sparse_mla_decode(
         ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse), _ptr(workspace), ws,
         _stream(stream)))
+
+
+def sparse_mla_decode_noalloc(dims: Dims, q, kv, idx, out, lse=None, stream=None) -> None:
+    _contig(q, kv, idx, out, lse)
+    _check_mla_sizes(dims, q, kv, idx, out, lse)
+    _check("dsa_sparse_mla_decode_noalloc", lib().dsa_sparse_mla_decode_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def prefill_chunk(dims: Dims, q, kv_chunk, q_idx, w_idx, k_idx_chunk, kv_cache, k_idx_cache, scores, ld: int,

@@ -62,5 +62,9 @@ constexpr int kDecodeTile = 32;           // slots per tile of the attention ker
 MlaSplit mla_decode_split(const MlaArgs& a);
 // Bytes of the partial outputs and log-sum-exps of a split launch (0 = no split).
 size_t mla_decode_workspace_bytes(const MlaArgs& a);
+// Size of the library's own decode scratch, used by the entry point that
+// allocates nothing: 32 MiB holds 255 split partials of 64 heads x 513 fp32
+// (e.g. up to 15 queries at 16 splits).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 
 }  // namespace dsa

@@ -92,6 +92,20 @@ dsa_status dsa_sparse_mla_decode(const dsa_dims* dims, const void* q, const void
   return from_hip(dsa::launch_mla_decode(a, workspace, s));
 }
 
+dsa_status dsa_sparse_mla_decode_noalloc(const dsa_dims* dims, const void* q, const void* kv_cache,
+                                         const int32_t* idx, float* out, float* lse, void* stream) {
+  dsa::MlaArgs a{};
+  dsa_status st = dsa::check_mla(dims, q, kv_cache, idx, out, lse, &a);
+  if (st != DSA_OK || dims->n_q == 0) return st;
+  const size_t need = dsa::mla_decode_workspace_bytes(a);
+  if (need > dsa::kDecodeScratchBytes) return DSA_ERR_WORKSPACE;  // beyond the library's scratch
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = ready(kMla, s)) != DSA_OK) return st;
+  void* ws = nullptr;
+  if (need > 0 && dsa::decode_scratch(&ws) != hipSuccess) return DSA_ERR_DEVICE;
+  return from_hip(dsa::launch_mla_decode(a, ws, s));
+}
+
 dsa_status dsa_prefill_chunk(const dsa_dims* dims, const void* q, const void* kv_chunk, const void* q_idx,
                              const float* w_idx, const void* k_idx_chunk, void* kv_cache, void* k_idx_cache,
                              float* scores, int64_t ld, int32_t* idx, float* out, float* lse, void* workspace,

@@ -27,6 +27,9 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
 hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t s);
+// Device address of the current device's copy of the library's decode
+// scratch (kDecodeScratchBytes), looked up once per device.
+hipError_t decode_scratch(void** ptr);
 
 // Launch-limit check of every fast-path kernel of a step on the current
 // device (block size, LDS, registers against what the launch needs), cached

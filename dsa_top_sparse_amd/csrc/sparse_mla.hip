@@ -28,6 +28,9 @@
 //             heads, reading V transposed out of the key-major stage.
 // The two roles run side by side on every SIMD, one tile apart, and meet at
 // one barrier per tile (details at the kernel).
+#include <mutex>
+#include <unordered_map>
+
 #include "common.h"
 #include "device_checks.h"
 #include "kernels.h"
@@ -823,6 +826,35 @@ hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t s) {
   if (e != hipSuccess) return e;
   return launch_kernel(mla_combine_kernel, dim3(a.n_q, kH), dim3(kCombineThreads), 0, s, a.n_q, sp.splits,
                        static_cast<const float*>(part_out), static_cast<const float*>(part_lse), a.out, a.lse);
+}
+
+// Library-owned scratch for callers that cannot allocate: the split partials
+// of a decode call (kDecodeScratchBytes, one copy per GPU, kept until the
+// process ends). Host code never uses this name as an address: the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+namespace {
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;  // device id -> that device's copy of `scratch`
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr.emplace(dev, p);
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {

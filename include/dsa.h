@@ -175,6 +175,29 @@ DSA_API dsa_status dsa_sparse_mla_decode(const dsa_dims *dims, const void *q, co
                                          size_t ws_bytes, void *stream);
 
 /*
+ * dsa_sparse_mla_decode_noalloc -- dsa_sparse_mla_decode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same operation, arguments and results as dsa_sparse_mla_decode with the
+ * workspace removed: the split partials go to a scratch array the library
+ * holds in device memory, 32 MiB on each GPU it runs on, kept until the
+ * process ends. Nothing is allocated or freed by this call. The scratch is
+ * that of the current device (the stream must belong to it); every call on a
+ * GPU shares it, so calls that overlap in time on one GPU race and must be
+ * ordered by the caller (one stream, or events). Nothing in it needs to start
+ * at zero: each call writes every partial it reads.
+ *
+ * Returns DSA_ERR_WORKSPACE, before anything is enqueued, when the partials
+ * would exceed the scratch (dsa_sparse_mla_decode_workspace_bytes(dims) >
+ * 32 MiB: more than 255 split partials of 64 heads x 513 fp32, e.g. more
+ * than 15 queries at 16 splits of a 2,048-slot index row); calls that need no
+ * split (dsa_sparse_mla_decode_workspace_bytes(dims) == 0) never touch it.
+ */
+DSA_API dsa_status dsa_sparse_mla_decode_noalloc(const dsa_dims *dims, const void *q, const void *kv_cache,
+                                                 const int32_t *idx, float *out, float *lse, void *stream);
+
+/*
  * dsa_prefill_chunk -- one chunk of a chunked prefill: the cache append that
  * precedes the hot path, then steps 1-7.
  *

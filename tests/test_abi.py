@@ -163,3 +163,18 @@ def test_decode_workspace_and_bad_arguments(L):
     assert call(dims(n_q=4, top_k=0)) == SHAPE
     assert call(d, out=None) == NULL
     assert call(dims(n_q=0), q=None, kv=None, idx=None, out=None, ws_ptr=None, ws_bytes=0) == OK
+
+
+def test_decode_noalloc_rejects_before_the_device(L):
+    def call(dd, **kw):
+        a = dict(q=FAKE, kv=FAKE, idx=FAKE, out=FAKE, lse=None)
+        a.update(kw)
+        return L.dsa_sparse_mla_decode_noalloc(ctypes.byref(dd), a["q"], a["kv"], a["idx"], a["out"], a["lse"], None)
+
+    # 16 queries x 16 splits of 128 slots: 256 partials of 64 x 513 fp32, past the 32 MiB scratch
+    assert L.dsa_sparse_mla_decode_workspace_bytes(ctypes.byref(dims(n_q=16, offset=40000))) > 32 << 20
+    assert call(dims(n_q=16, offset=40000)) == WS
+    assert call(dims(n_q=4), out=None) == NULL
+    assert call(dims(n_q=4), lse=FAKE + 4) == ALIGN
+    assert call(dims(n_q=4, top_k=0)) == SHAPE
+    assert call(dims(n_q=0), q=None, kv=None, idx=None, out=None) == OK
