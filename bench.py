@@ -71,49 +71,107 @@ def measured_traffic(kernel_file: str, workload: str):
     return r.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inputs, target_s: float):
+    """The oracle (untuned) on the host cores, on a bounded sample of the same
+    chunk's query rows: all three steps timed one after the other; plus the
+    tiny workload on one core."""
     import numpy as np
     import oracle
+    from dsa_top_sparse_amd import synth
     oracle.build(force=False)
+
+    def staged(c, inp, rows):
+        t = [time.perf_counter()]
+        s = oracle.indexer_scores(c.n_q, c.offset, inp["qidx"], inp["w"], inp["kidx"], rows=rows)
+        t.append(time.perf_counter())
+        idx = oracle.topk_select(c.n_q, c.offset, c.top_k, s, rows=rows)
+        t.append(time.perf_counter())
+        oracle.sparse_mla(c.n_q, c.offset, c.sm_scale, c.d_latent, inp["q"], inp["kv"], idx, rows=rows)
+        t.append(time.perf_counter())
+        return [t[i + 1] - t[i] for i in range(3)]
+
     spread = np.linspace(0, cfg.n_q - 1, 16).astype(int).tolist()
-    oracle.full_path(cfg, inputs, rows=spread[:2])  # warm-up: thread pool, first-touch pages
-    t0 = time.perf_counter()
-    oracle.full_path(cfg, inputs, rows=spread)
-    t_cal = time.perf_counter() - t0
+    staged(cfg, inputs, spread[:2])  # warm-up: thread pool, first-touch pages
+    t_cal = sum(staged(cfg, inputs, spread))
     n_rows = int(max(16, min(cfg.n_q, round(16 * target_s / max(t_cal, 1e-3)))))
     rows = np.linspace(0, cfg.n_q - 1, n_rows).astype(int).tolist()
-    t0 = time.perf_counter()
-    oracle.full_path(cfg, inputs, rows=rows)
-    t = time.perf_counter() - t0
-    return {"value": len(rows) / t, "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{len(rows)} evenly spaced query rows of the same chunk (all three steps), {t:.1f} s"}
+    st = staged(cfg, inputs, rows)
+    t = sum(st)
+    cores = oracle.num_threads()
+    # the tiny fp32 workload, every row, on one core
+    c0 = synth.CONFIGS["C0"]
+    c0_in = synth.generate(c0)
+    oracle.set_threads(1)
+    try:
+        t0 = sum(staged(c0, c0_in, None))
+    finally:
+        oracle.set_threads(cores)
+    return {"value": round(len(rows) / t, 2), "unit": UNIT, "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} evenly spaced query rows of the same chunk, all three steps, {t:.1f} s",
+            "cpu_model": cpu_model(),
+            "stage_s": {"indexer": round(st[0], 3), "select": round(st[1], 3), "attention": round(st[2], 3)},
+            "one_core_tiny": {"workload": c0.name, "rows": c0.n_q, "s": round(t0, 4),
+                              "value": round(c0.n_q / t0, 1), "unit": UNIT}}
+
+
+# The pages' per-layer rate for the same replay (8,192 tokens in 2,048-token
+# chunks, DSA core + indexer, M5 Ultra; BASELINE.md): context, not a target.
+PAGES_M5_CORE_INDEXER_QTOK_S = 33499.0
+
+
+def _time_replay(torch, pcfg, pdev, chunk, outs, scores, stream, reps):
+    from dsa_top_sparse_amd import prefill
+    prefill.run_prefill(pcfg, pdev, chunk, outs, scores=scores, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        prefill.run_prefill(pcfg, pdev, chunk, outs, scores=scores, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def prefill_replay(torch, cfg, dev, stream, reps: int = 5):
-    """The pages' 8,192-token prefill from empty caches, in 2,048-token chunks
-    (dsa_prefill_chunk: cache append + the three steps per chunk), and as one
-    8,192-token chunk. Reuses the bench workload's first 8,192 rows as the
-    prompt (same shapes and distributions)."""
-    from dsa_top_sparse_amd import prefill, synth
+    """The pages' prompts from empty caches through dsa_prefill_chunk (cache
+    append + the three steps per chunk): 8,192 tokens (the bench workload's
+    first 8,192 rows) and the 17,536-token prompt, each in 2,048- and
+    8,192-token chunks."""
+    from dsa_top_sparse_amd import binding, prefill, synth
+    res = {}
     T = 8192
-    pcfg = synth.PROMPTS["P8K"]
     pdev = {"q": dev["q"][:T], "qidx": dev["qidx"][:T], "w": dev["w"][:T], "kv": dev["kv"][:T].contiguous(),
             "kidx": dev["kidx"][:T].contiguous()}
-    outs = prefill.alloc_prompt_outputs(pcfg)
-    scores = torch.empty((T, T), dtype=torch.float32, device="cuda")
-    res = {"workload": "8,192-token prompt from empty caches (chunked prefill, cache append included)"}
-    for chunk in (2048, 8192):
-        prefill.run_prefill(pcfg, pdev, chunk, outs, scores=scores, stream=stream)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            prefill.run_prefill(pcfg, pdev, chunk, outs, scores=scores, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        res[f"chunk{chunk}"] = {"ms": round(ms, 4), "query_tokens_per_s": round(T / ms * 1e3, 1),
-                                "chunks": (T + chunk - 1) // chunk}
+    jobs = [("P8K", synth.PROMPTS["P8K"], pdev)]
+    p17 = synth.PROMPTS["P17K"]
+    jobs.append(("P17K", p17, None))
+    for name, pcfg, pd in jobs:
+        if pd is None:
+            pd = binding.to_device(synth.generate(pcfg))
+        T = pcfg.n_q
+        outs = prefill.alloc_prompt_outputs(pcfg)
+        scores = torch.empty((T, T), dtype=torch.float32, device="cuda")
+        r = {"workload": f"{T:,}-token prompt from empty caches (cache append included)"}
+        for chunk in (2048, 8192):
+            ms = _time_replay(torch, pcfg, pd, chunk, outs, scores, stream, reps)
+            r[f"chunk{chunk}"] = {"ms": round(ms, 4), "query_tokens_per_s": round(T / ms * 1e3, 1),
+                                  "chunks": (T + chunk - 1) // chunk}
+        if name == "P8K":
+            r["pages_m5_ultra_2k_chunks_query_tokens_per_s"] = PAGES_M5_CORE_INDEXER_QTOK_S
+        res[name] = r
+        del outs, scores, pd
+        torch.cuda.empty_cache()
     return res
 
 
@@ -159,6 +217,71 @@ def decode_steps(torch, cfg, dev, stream, reps: int = 20):
     return res
 
 
+def time_workload(torch, binding, cfg, dev, outs, stream, steps, warmup, flush):
+    """Per-kernel HIP-event times (ms) of `steps` steps after `warmup` untimed
+    ones, on the launch stream. Warm: the steps run back to back in one
+    synchronised bracket (wall = that bracket). With `flush`, a buffer is
+    overwritten before every step, outside the events and the wall clock."""
+    dims = binding.make_dims(cfg)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        binding.indexer_scores(dims, dev["qidx"], dev["w"], dev["kidx"], outs["scores"], outs["ld"], stream)
+        if ev:
+            ev[1].record(stream)
+        binding.topk_select(dims, outs["scores"], outs["ld"], outs["idx"], outs["workspace"], stream)
+        if ev:
+            ev[2].record(stream)
+        binding.sparse_mla_fwd(dims, dev["q"], dev["kv"], outs["idx"], outs["out"], outs["lse"], stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    if flush is None:
+        t0 = time.perf_counter()
+        for s in range(steps):
+            step(events[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        wall = 0.0
+        for s in range(steps):
+            flush.fill_(float(s))
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step(events[s])
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+    k_ms = {"indexer": [], "topk": [], "attention": []}
+    for ev in events:
+        k_ms["indexer"].append(ev[0].elapsed_time(ev[1]))
+        k_ms["topk"].append(ev[1].elapsed_time(ev[2]))
+        k_ms["attention"].append(ev[2].elapsed_time(ev[3]))
+    return {"wall": wall, "avg": {k: sum(v) / len(v) for k, v in k_ms.items()},
+            "med": {k: sorted(v)[len(v) // 2] for k, v in k_ms.items()},
+            "min": {k: min(v) for k, v in k_ms.items()}}
+
+
+def kernel_summary(cfg, avg):
+    """Per-kernel time and fraction of its roofline from average launch times (ms)."""
+    w_idx, w_topk, w_attn = algorithmic_work(cfg)
+    t_attn = avg["attention"] * 1e-3
+    return {
+        "indexer": {"ms": round(avg["indexer"], 4), "bound": "hbm",
+                    "hbm_frac": round(w_idx["bytes"] / (avg["indexer"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "mfma_frac": round(w_idx["flops"] / (avg["indexer"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "topk": {"ms": round(avg["topk"], 4), "bound": "hbm",
+                 "hbm_frac": round(w_topk["bytes"] / (avg["topk"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "attention": {"ms": round(avg["attention"], 4), "bound": "mfma",
+                      "mfma_frac": round(w_attn["flops"] / t_attn / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "gather_GBs": round(w_attn["gathered_bytes"] / t_attn / 1e9, 1)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,10 +289,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C3", help="workload id C0..C4 (default: 8k chunk at offset 8k)")
     ap.add_argument("--cold", action="store_true", help="overwrite a 1 GiB buffer before each step (MALL/L2 flush)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="steps timed again after the warm ones with L2 and MALL flushed before each (0 = skip)")
     ap.add_argument("--cpu-baseline-s", type=float, default=18.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-replay", dest="replay", action="store_false",
-                    help="skip the side measurements: chunked-prefill replay (8,192 tokens from empty caches in "
-                         "2,048-token chunks) and decode steps")
+                    help="skip the side measurements: the other workloads, chunked-prefill replays of the pages' "
+                         "prompts, and decode steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference kernel for the HBM byte counters)")
     args = ap.parse_args()
@@ -193,19 +318,6 @@ def main():
     stream = torch.cuda.current_stream()
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.cold else None
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        binding.indexer_scores(dims, dev["qidx"], dev["w"], dev["kidx"], outs["scores"], outs["ld"], stream)
-        if ev:
-            ev[1].record(stream)
-        binding.topk_select(dims, outs["scores"], outs["ld"], outs["idx"], outs["workspace"], stream)
-        if ev:
-            ev[2].record(stream)
-        binding.sparse_mla_fwd(dims, dev["q"], dev["kv"], outs["idx"], outs["out"], outs["lse"], stream)
-        if ev:
-            ev[3].record(stream)
-
     if args.copy_calibration:
         # A plain device copy of known size: its rocprofv3 FETCH_SIZE / WRITE_SIZE
         # give the scale factor between counter readings and bytes moved.
@@ -215,35 +327,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    if flush is None:
-        # warm: the K steps run back to back inside one synchronised bracket
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            step(events[s])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        # cold: a 1 GiB write evicts L2 and MALL before each step, outside the timed brackets
-        wall = 0.0
-        for s in range(args.steps):
-            flush.fill_(float(s))
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            step(events[s])
-            torch.cuda.synchronize()
-            wall += time.perf_counter() - t0
-    k_ms = {"indexer": [], "topk": [], "attention": []}
-    for ev in events:
-        k_ms["indexer"].append(ev[0].elapsed_time(ev[1]))
-        k_ms["topk"].append(ev[1].elapsed_time(ev[2]))
-        k_ms["attention"].append(ev[2].elapsed_time(ev[3]))
-    avg = {k: sum(v) / len(v) for k, v in k_ms.items()}
+    timing = time_workload(torch, binding, cfg, dev, outs, stream, args.steps, args.warmup, flush)
+    wall = timing["wall"]
+    avg, med, mn = timing["avg"], timing["med"], timing["min"]
     ms_per_step = 1e3 * wall / args.steps
 
     w_idx, w_topk, w_attn = algorithmic_work(cfg)
@@ -254,20 +340,34 @@ def main():
                 "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "mla_mfma_kernel", "flops_per_launch": w_attn["flops"],
                 "avg_launch_ms": round(avg["attention"], 4)}
-    med = {k: sorted(v)[len(v) // 2] for k, v in k_ms.items()}
-    mn = {k: min(v) for k, v in k_ms.items()}
-    kernels = {
-        "indexer": {"ms": round(avg["indexer"], 4), "bound": "hbm",
-                    "hbm_frac": round(w_idx["bytes"] / (avg["indexer"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                    "mfma_frac": round(w_idx["flops"] / (avg["indexer"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-        "topk": {"ms": round(avg["topk"], 4), "bound": "hbm",
-                 "hbm_frac": round(w_topk["bytes"] / (avg["topk"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "attention": {"ms": round(avg["attention"], 4), "bound": "mfma", "mfma_frac": roofline["frac"],
-                      "gather_GBs": round(w_attn["gathered_bytes"] / t_attn / 1e9, 1)},
-    }
+    kernels = kernel_summary(cfg, avg)
     for k in kernels:
         kernels[k]["median_ms"] = round(med[k], 4)
         kernels[k]["min_ms"] = round(mn[k], 4)
+    if flush is None and args.cold_steps > 0:
+        # the HBM-bound steps with L2 and MALL flushed before every step
+        big = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold = time_workload(torch, binding, cfg, dev, outs, stream, args.cold_steps, 0, big)
+        del big
+        cold_k = kernel_summary(cfg, cold["avg"])
+        for k in ("indexer", "topk"):
+            kernels[k]["cold_ms"] = cold_k[k]["ms"]
+            kernels[k]["cold_hbm_frac"] = cold_k[k]["hbm_frac"]
+        kernels["attention"]["cold_ms"] = cold_k["attention"]["ms"]
+        kernels["attention"]["cold_mfma_frac"] = cold_k["attention"]["mfma_frac"]
+    workloads = None
+    if args.replay:
+        workloads = {}
+        for other in ("C2", "C4"):
+            ocfg = synth.CONFIGS[other]
+            odev = binding.to_device(synth.generate(ocfg))
+            oouts = binding.alloc_outputs(ocfg)
+            t = time_workload(torch, binding, ocfg, odev, oouts, stream, 10, 3, None)
+            workloads[ocfg.name] = {"ms_per_step": round(1e3 * t["wall"] / 10, 4),
+                                    "query_tokens_per_s": round(ocfg.n_q * 10 / t["wall"], 1),
+                                    "kernels": kernel_summary(ocfg, t["avg"])}
+            del odev, oouts
+            torch.cuda.empty_cache()
     replay = prefill_replay(torch, cfg, dev, stream) if args.replay else None
     decode = decode_steps(torch, cfg, dev, stream) if args.replay else None
     cpu = None
@@ -283,6 +383,8 @@ def main():
                    "indexer": f"{cfg.n_idx_heads}x{cfg.d_idx}", "mode": "cold" if args.cold else "warm"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
+    if workloads is not None:
+        line["workloads"] = workloads
     if replay is not None:
         line["prefill_replay"] = replay
     if decode is not None:

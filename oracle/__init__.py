@@ -59,12 +59,18 @@ def _load():
         for f in (lib.oracle_indexer_scores, lib.oracle_topk_select, lib.oracle_sparse_mla):
             f.restype = i32
         lib.oracle_num_threads.restype = i32
+        lib.oracle_set_threads.argtypes = [i32]
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _dtype_code(a: np.ndarray) -> int:

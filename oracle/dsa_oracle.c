@@ -205,3 +205,14 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the parallel loops that follow (a timing knob; results do not
+ * depend on it: every row is computed by one thread in a fixed order). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
