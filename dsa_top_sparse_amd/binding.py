@@ -21,6 +21,8 @@ EXPORTED = (
     "dsa_indexer_scores",
     "dsa_topk_workspace_bytes",
     "dsa_topk_select",
+    "dsa_indexer_topk_workspace_bytes",
+    "dsa_indexer_topk",
     "dsa_sparse_mla_fwd",
     "dsa_prefill_chunk",
     "dsa_sparse_mla_decode_workspace_bytes",
@@ -78,12 +80,15 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk_workspace_bytes.restype = sz
         L.dsa_topk_select.argtypes = [dp, vp, i64, vp, vp, sz, vp]
         L.dsa_sparse_mla_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+        L.dsa_indexer_topk_workspace_bytes.argtypes = [dp]
+        L.dsa_indexer_topk_workspace_bytes.restype = sz
+        L.dsa_indexer_topk.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
         L.dsa_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
         L.dsa_sparse_mla_decode_workspace_bytes.argtypes = [dp]
         L.dsa_sparse_mla_decode_workspace_bytes.restype = sz
         L.dsa_sparse_mla_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dsa_sparse_mla_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp]
-        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk,
+        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_indexer_topk, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk,
                   L.dsa_sparse_mla_decode, L.dsa_sparse_mla_decode_noalloc):
             f.restype = ctypes.c_int
         L.dsa_self_test.argtypes = []
@@ -205,6 +210,24 @@ def topk_select(dims: Dims, scores, ld: int, idx, workspace=None, stream=None) -
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_topk_select", lib().dsa_topk_select(
         ctypes.byref(dims), _ptr(scores), int(ld), _ptr(idx), _ptr(workspace), ws,
+        _stream(stream)))
+
+
+def indexer_topk_workspace_bytes(dims: Dims) -> int:
+    return int(lib().dsa_indexer_topk_workspace_bytes(ctypes.byref(dims)))
+
+
+def indexer_topk(dims: Dims, q_idx, w_idx, k_idx, idx, workspace, stream=None) -> None:
+    """Indexer scores and top-k select in one call, without the score matrix."""
+    _contig(q_idx, w_idx, k_idx, idx, workspace)
+    if dims.n_q > 0:
+        _fits(q_idx, dims.n_q * dims.n_idx_heads * dims.d_idx, _idx_size(dims), "q_idx")
+        _fits(w_idx, dims.n_q * dims.n_idx_heads, 4, "w_idx")
+        _fits(k_idx, (dims.offset + dims.n_q) * dims.d_idx, _idx_size(dims), "k_idx_cache")
+        _fits(idx, dims.n_q * dims.top_k, 4, "idx")
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_indexer_topk", lib().dsa_indexer_topk(
+        ctypes.byref(dims), _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(idx), _ptr(workspace), ws,
         _stream(stream)))
 
 

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa_amd.so")
-SOURCES = ["dsa_api.cpp", "validate.cpp", "selftest.hip", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["dsa_api.cpp", "validate.cpp", "selftest.hip", "indexer.hip", "topk.hip", "fused.hip", "sparse_mla.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -62,6 +62,33 @@ constexpr int kDecodeTile = 32;           // slots per tile of the attention ker
 MlaSplit mla_decode_split(const MlaArgs& a);
 // Bytes of the partial outputs and log-sum-exps of a split launch (0 = no split).
 size_t mla_decode_workspace_bytes(const MlaArgs& a);
+// How the MFMA indexer splits a chunk of n_q queries over ld keys: 64-query
+// blocks times ranges of keys_per_unit keys (n_kr of them).
+struct IndexerUnits {
+  int n_qb;
+  int keys_per_unit;
+  int64_t n_kr;
+};
+IndexerUnits indexer_units(int n_q, int64_t ld);
+
+// Workspace of the fused indexer + select (dsa_indexer_topk). With `fused`
+// (bf16 4 x 128 indexer, at most kFusedMaxRow keys, top_k <= kFusedMaxTopk),
+// the byte offsets of its arrays; otherwise one [n_q][scores_ld] score matrix
+// for the unfused kernels. Every array starts 256-byte aligned.
+constexpr int kFusedMaxRow = 65536;  // candidate key indices are 16-bit in LDS
+constexpr int kFusedMaxTopk = 4096;  // the select's LDS candidate capacity
+constexpr int kFusedSample = 2048;   // keys of each query's threshold sample
+struct FusedLayout {
+  bool fused;
+  size_t bytes;
+  size_t tau_off, tf_off, counts_off, sample_off, cand_off;
+  int64_t row_cap, n_kr;
+  int keys_per_unit;
+  size_t scores_off;
+  int64_t scores_ld;
+};
+FusedLayout fused_layout(int n_q, int offset, int n_idx_heads, int d_idx, bool idx_bf16, int top_k);
+
 // Size of the library's own decode scratch, used by the entry point that
 // allocates nothing: 32 MiB holds 255 split partials of 64 heads x 513 fp32
 // (e.g. up to 15 queries at 16 splits).

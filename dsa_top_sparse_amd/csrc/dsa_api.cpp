@@ -13,7 +13,7 @@ dsa_status from_hip(hipError_t e) {
   return e == hipErrorInvalidConfiguration ? DSA_ERR_UNSUPPORTED : DSA_ERR_DEVICE;
 }
 
-enum Step { kIndexer = 1, kTopk = 2, kMla = 4 };
+enum Step { kIndexer = 1, kTopk = 2, kMla = 4, kFused = 8 };
 
 // The checks that must pass before the first launch of the given steps on
 // this device: the launch limits of their kernels and, unless the stream is
@@ -25,6 +25,7 @@ dsa_status ready(int steps, hipStream_t s) {
   if ((steps & kIndexer) && e == hipSuccess) e = dsa::check_indexer_kernels();
   if ((steps & kTopk) && e == hipSuccess) e = dsa::check_topk_kernels();
   if ((steps & kMla) && e == hipSuccess) e = dsa::check_mla_kernels();
+  if ((steps & kFused) && e == hipSuccess) e = dsa::check_fused_kernels();
   if (e != hipSuccess) return from_hip(e);
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cap) != hipSuccess) return DSA_ERR_DEVICE;
@@ -60,6 +61,27 @@ dsa_status dsa_topk_select(const dsa_dims* dims, const float* scores, int64_t ld
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = ready(kTopk, s)) != DSA_OK) return st;
   return from_hip(dsa::launch_topk(a, s));
+}
+
+size_t dsa_indexer_topk_workspace_bytes(const dsa_dims* dims) {
+  if (!dims || dims->n_q <= 0 || dims->offset < 0 || (int64_t)dims->offset + dims->n_q > 0x7fffffffLL ||
+      dims->top_k < 1 || dims->top_k > dsa::kTopkMax || dims->n_idx_heads <= 0 || dims->d_idx <= 0)
+    return 0;
+  return dsa::fused_layout(dims->n_q, dims->offset, dims->n_idx_heads, dims->d_idx, dims->idx_dtype == DSA_BF16,
+                           dims->top_k)
+      .bytes;
+}
+
+dsa_status dsa_indexer_topk(const dsa_dims* dims, const void* q_idx, const float* w_idx, const void* k_idx_cache,
+                            int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
+  dsa::IndexerArgs ia{};
+  dsa::TopkArgs ta{};
+  dsa::FusedLayout L{};
+  dsa_status st = dsa::check_indexer_topk(dims, q_idx, w_idx, k_idx_cache, idx, workspace, ws_bytes, &ia, &ta, &L);
+  if (st != DSA_OK || dims->n_q == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = ready(kIndexer | kTopk | (L.fused ? kFused : 0), s)) != DSA_OK) return st;
+  return from_hip(dsa::launch_indexer_topk(ia, ta, L, workspace, s));
 }
 
 dsa_status dsa_sparse_mla_fwd(const dsa_dims* dims, const void* q, const void* kv_cache, const int32_t* idx,

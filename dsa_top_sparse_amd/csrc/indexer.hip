@@ -179,10 +179,16 @@ constexpr int kIdxRowBytes = 256;  // 128 bf16
 constexpr int kIdx8Threads = 512;  // indexer_lds_kernel: 8 waves of 8 queries
 constexpr int kTbRow = 36;         // floats per row of a wave's score tile (32 keys + pad)
 
-__global__ __launch_bounds__(kIdx8Threads) void indexer_lds_kernel(
+// FILTER: instead of the score matrix, every causal score >= the query's
+// threshold is written with its key index to the query's candidate segment of
+// this key range (in key order, at most keys_per_unit of them), and the count
+// per (query, key range) to counts; the scores are the same, computed the
+// same way. Queries with no more causal keys than top_k write nothing.
+template <bool FILTER>
+__global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4))) void indexer_lds_kernel(
     int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
-    int n_units, int units_per_xcd, int keys_per_unit) {
+    int n_units, int units_per_xcd, int keys_per_unit, IndexerCandidates fo) {
   constexpr int D = 128, KS = D / 16;
   const int bid = blockIdx.x;
   const int u = (bid & 7) * units_per_xcd + (bid >> 3);
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(kIdx8Threads) void indexer_lds_kernel(
   const int64_t t_ctx = (int64_t)offset + n_q;
   const int64_t p_max = (int64_t)offset + q0 + nrows - 1;
   if (k_begin > p_max) {  // every key of the range lies beyond every query of the block
-    fill_neg_inf(scores, ld, q0, nrows, k_begin, k_end);
+    if (!FILTER) fill_neg_inf(scores, ld, q0, nrows, k_begin, k_end);
     return;
   }
   // keys [k_begin, k_comp) need the product; [k_comp, k_end) are past every query
@@ -246,6 +252,22 @@ __global__ __launch_bounds__(kIdx8Threads) void indexer_lds_kernel(
       a[mb][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // FILTER: per query pair g (queries 2 g and 2 g + 1 of the wave's eight,
+  // held by the lower and the upper half-wave) the two thresholds (+inf where
+  // nothing is written), segment offsets and running counts, all wave-uniform.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  float tf_lo[4], tf_hi[4];
+  uint32_t seg_lo[4], seg_hi[4], cnt_lo[4] = {0u, 0u, 0u, 0u}, cnt_hi[4] = {0u, 0u, 0u, 0u};
+  if (FILTER) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = wave_u * 8 + 2 * g;
+      tf_lo[g] = (r0 < nrows && (int64_t)offset + q0 + r0 + 1 > fo.top_k) ? fo.tf[q0 + r0] : INFINITY;
+      tf_hi[g] = (r0 + 1 < nrows && (int64_t)offset + q0 + r0 + 2 > fo.top_k) ? fo.tf[q0 + r0 + 1] : INFINITY;
+      seg_lo[g] = static_cast<uint32_t>((int64_t)(q0 + r0) * fo.row_cap + (int64_t)kr * keys_per_unit);
+      seg_hi[g] = seg_lo[g] + static_cast<uint32_t>(fo.row_cap);
+    }
+  }
   u32x4 pre[2];
   load_stage(0, pre);
   store_stage(0, pre);
@@ -279,6 +301,30 @@ __global__ __launch_bounds__(kIdx8Threads) void indexer_lds_kernel(
       // negative int32); adding +0 turns a -0 sum into +0;
       // the causal mask is needed only where the block reaches the wave's
       // first query (block-uniform test).
+      if (FILTER) {
+        // the lane's causal scores >= its query's threshold, in key order,
+        // to that query's segment of this key range
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qrow = wave * 8 + 2 * g + hi;
+          float sc = 0.0f;
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            sc = fmaf(sw[qrow][h], __int_as_float(max(__float_as_int(acc[0][4 * g + h]), 0)), sc);
+          sc = sc + 0.0f;
+          const bool keep = key <= (int64_t)offset + q0 + qrow && sc >= (hi ? tf_hi[g] : tf_lo[g]);
+          const uint64_t m = __ballot(keep);
+          const uint32_t m_lo = static_cast<uint32_t>(m), m_hi = static_cast<uint32_t>(m >> 32);
+          if (keep) {
+            const uint32_t at = (hi ? seg_hi[g] + cnt_hi[g] : seg_lo[g] + cnt_lo[g]) +
+                                __builtin_popcount((hi ? m_hi : m_lo) & ((1u << l32) - 1u));
+            fo.cand[at] = uint2{__float_as_uint(sc), static_cast<uint32_t>(key)};
+          }
+          cnt_lo[g] += __builtin_popcount(m_lo);
+          cnt_hi[g] += __builtin_popcount(m_hi);
+        }
+        continue;
+      }
       const bool all_causal = nb + 31 <= (int64_t)offset + q0 + wave * 8;
       const bool all_in = nb + 32 <= k_end && q0 + wave * 8 + 8 <= n_q;  // every row and key of the sub-block exists
       if (vec_ok && all_in) {
@@ -333,6 +379,15 @@ __global__ __launch_bounds__(kIdx8Threads) void indexer_lds_kernel(
       __syncthreads();
     }
   }
+  if (FILTER) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qrow = wave * 8 + 2 * g + hi;
+      if (l32 == 0 && qrow < nrows)
+        fo.counts[(int64_t)(q0 + qrow) * fo.n_kr + kr] = static_cast<int32_t>(hi ? cnt_hi[g] : cnt_lo[g]);
+    }
+    return;
+  }
   // Keys past every query of the block: the 32-key blocks above wrote up to
   // the first multiple of 32 at or after k_comp (masked to -inf per row).
   const int64_t written = min<int64_t>(k_end, k_begin + 32 * ((k_comp - k_begin + 31) / 32));
@@ -342,22 +397,18 @@ __global__ __launch_bounds__(kIdx8Threads) void indexer_lds_kernel(
 
 template <int D>
 hipError_t launch_mfma(const IndexerArgs& a, hipStream_t s) {
-  const int n_qb = (a.n_q + kIdxQueries - 1) / kIdxQueries;
-  // Aim for >= 2048 workgroups (8 per CU) with 32-key-aligned ranges.
-  int64_t target_ranges = (2048 + n_qb - 1) / n_qb;
-  int64_t kpu = (a.ld + target_ranges - 1) / target_ranges;
-  kpu = ((kpu + 63) / 64) * 64;
-  if (kpu < 128) kpu = 128;
-  if (kpu > 1024) kpu = 1024;
-  const int64_t n_kr = (a.ld + kpu - 1) / kpu;
+  const IndexerUnits un = indexer_units(a.n_q, a.ld);
+  const int n_qb = un.n_qb;
+  const int64_t kpu = un.keys_per_unit;
+  const int64_t n_kr = un.n_kr;
   const int64_t n_units = n_kr * n_qb;
   if (n_units > (int64_t)1 << 30) return hipErrorInvalidValue;
   const int units_per_xcd = (int)((n_units + 7) / 8);
   const int grid = units_per_xcd * 8;
   if (D == 128 && kpu % kIdxStageKeys == 0)
-    return launch_kernel(indexer_lds_kernel, dim3(grid), dim3(kIdx8Threads), 0, s, a.n_q, a.offset,
+    return launch_kernel(indexer_lds_kernel<false>, dim3(grid), dim3(kIdx8Threads), 0, s, a.n_q, a.offset,
                          static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx), a.scores,
-                         a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
+                         a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu, IndexerCandidates{});
   return launch_kernel(indexer_mfma_kernel<D>, dim3(grid), dim3(kIdxThreads), 0, s, a.n_q, a.offset,
                        static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx), a.scores,
                        a.ld, n_qb, (int)n_units, units_per_xcd, (int)kpu);
@@ -369,7 +420,8 @@ hipError_t check_indexer_kernels_now() {
     int threads;
     size_t dyn_lds;
   } ks[] = {
-      {reinterpret_cast<const void*>(indexer_lds_kernel), kIdx8Threads, 0},
+      {reinterpret_cast<const void*>(indexer_lds_kernel<false>), kIdx8Threads, 0},
+      {reinterpret_cast<const void*>(indexer_lds_kernel<true>), kIdx8Threads, 0},
       {reinterpret_cast<const void*>(indexer_mfma_kernel<32>), kIdxThreads, 0},
       {reinterpret_cast<const void*>(indexer_mfma_kernel<64>), kIdxThreads, 0},
       {reinterpret_cast<const void*>(indexer_mfma_kernel<128>), kIdxThreads, 0},
@@ -389,6 +441,19 @@ hipError_t check_indexer_kernels_now() {
 hipError_t check_indexer_kernels() {
   static PerDeviceCache cache;
   return once_per_device(cache, check_indexer_kernels_now);
+}
+
+hipError_t launch_indexer_candidates(const IndexerArgs& a, const IndexerCandidates& fo, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  const IndexerUnits un = indexer_units(a.n_q, a.ld);
+  const int64_t n_units = un.n_kr * un.n_qb;
+  if (n_units > (int64_t)1 << 30 || un.keys_per_unit % kIdxStageKeys != 0 || fo.n_kr != un.n_kr ||
+      fo.row_cap != un.n_kr * un.keys_per_unit)
+    return hipErrorInvalidValue;
+  const int units_per_xcd = (int)((n_units + 7) / 8);
+  return launch_kernel(indexer_lds_kernel<true>, dim3(units_per_xcd * 8), dim3(kIdx8Threads), 0, s, a.n_q, a.offset,
+                       static_cast<const uint16_t*>(a.q_idx), a.w, static_cast<const uint16_t*>(a.k_idx),
+                       static_cast<float*>(nullptr), a.ld, un.n_qb, (int)n_units, units_per_xcd, un.keys_per_unit, fo);
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {

@@ -65,6 +65,52 @@ size_t mla_decode_workspace_bytes(const MlaArgs& a) {
   return (size_t)sp.splits * (size_t)a.n_q * (size_t)a.n_heads * (size_t)(a.d_latent + 1) * sizeof(float);
 }
 
+IndexerUnits indexer_units(int n_q, int64_t ld) {
+  const int n_qb = (n_q + 63) / 64;
+  // Aim for >= 2048 workgroups (8 per CU) with 64-key-aligned ranges.
+  const int64_t target_ranges = (2048 + n_qb - 1) / n_qb;
+  int64_t kpu = (ld + target_ranges - 1) / target_ranges;
+  kpu = ((kpu + 63) / 64) * 64;
+  if (kpu < 128) kpu = 128;
+  if (kpu > 1024) kpu = 1024;
+  return IndexerUnits{n_qb, static_cast<int>(kpu), (ld + kpu - 1) / kpu};
+}
+
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+}  // namespace
+
+FusedLayout fused_layout(int n_q, int offset, int n_idx_heads, int d_idx, bool idx_bf16, int top_k) {
+  FusedLayout L{};
+  const int64_t t_ctx = static_cast<int64_t>(offset) + n_q;
+  const IndexerUnits un = indexer_units(n_q, t_ctx);
+  const int64_t row_cap = un.n_kr * un.keys_per_unit;
+  L.fused = idx_bf16 && n_idx_heads == 4 && d_idx == 128 && t_ctx <= kFusedMaxRow && top_k <= kFusedMaxTopk &&
+            static_cast<int64_t>(n_q) * row_cap < (int64_t(1) << 32);
+  if (L.fused) {
+    size_t o = 0;
+    L.tau_off = o;
+    o = align256(o + 4 * static_cast<size_t>(n_q));
+    L.tf_off = o;
+    o = align256(o + 4 * static_cast<size_t>(n_q));
+    L.counts_off = o;
+    o = align256(o + 4 * static_cast<size_t>(n_q) * static_cast<size_t>(un.n_kr));
+    L.sample_off = o;
+    o = align256(o + 4 * static_cast<size_t>(n_q) * kFusedSample);
+    L.cand_off = o;
+    o = align256(o + 8 * static_cast<size_t>(n_q) * static_cast<size_t>(row_cap));
+    L.bytes = o;
+    L.row_cap = row_cap;
+    L.n_kr = un.n_kr;
+    L.keys_per_unit = un.keys_per_unit;
+  } else {
+    L.scores_ld = (t_ctx + 3) & ~int64_t(3);
+    L.scores_off = 0;
+    L.bytes = align256(4 * static_cast<size_t>(n_q) * static_cast<size_t>(L.scores_ld));
+  }
+  return L;
+}
+
 dsa_status check_indexer(const dsa_dims* dims, const void* q_idx, const float* w_idx, const void* k_idx_cache,
                          float* scores, int64_t ld, IndexerArgs* a) {
   dsa_status st = check_chunk(dims);
@@ -119,6 +165,24 @@ dsa_status check_mla(const dsa_dims* dims, const void* q, const void* kv_cache, 
       return DSA_ERR_UNSUPPORTED;
   }
   return DSA_OK;
+}
+
+dsa_status check_indexer_topk(const dsa_dims* dims, const void* q_idx, const float* w_idx, const void* k_idx_cache,
+                              int32_t* idx, const void* workspace, size_t ws_bytes, IndexerArgs* ia, TopkArgs* ta,
+                              FusedLayout* layout) {
+  dsa_status st = check_chunk(dims);
+  if (st != DSA_OK) return st;
+  const int64_t t_ctx = static_cast<int64_t>(dims->offset) + dims->n_q;
+  // the indexer's checks with the workspace standing in for the score matrix
+  // (pointers checked below), then the select's
+  st = check_indexer(dims, q_idx, w_idx, k_idx_cache, reinterpret_cast<float*>(16), t_ctx, ia);
+  if (st != DSA_OK) return st;
+  st = check_topk(dims, reinterpret_cast<const float*>(16), t_ctx, idx, 0, ta);
+  if (st != DSA_OK) return st;
+  if (dims->n_q == 0) return DSA_OK;
+  *layout = fused_layout(dims->n_q, dims->offset, dims->n_idx_heads, dims->d_idx, dims->idx_dtype == DSA_BF16,
+                         dims->top_k);
+  return check_workspace(workspace, ws_bytes, layout->bytes);
 }
 
 size_t act_row_bytes(const dsa_dims* dims) { return dtype_bytes(dims->act_dtype) * (size_t)(dims->d_latent + dims->d_rope); }

@@ -23,6 +23,13 @@ dsa_status check_append(const dsa_dims* dims, const void* kv_chunk, const void* 
 // `need` bytes (need == 0 accepts anything).
 dsa_status check_workspace(const void* workspace, size_t ws_bytes, size_t need);
 
+// The fused indexer + select: the indexer's and the select's checks (no score
+// matrix argument), the output and the workspace; fills both steps' arguments
+// and the workspace layout.
+dsa_status check_indexer_topk(const dsa_dims* dims, const void* q_idx, const float* w_idx, const void* k_idx_cache,
+                              int32_t* idx, const void* workspace, size_t ws_bytes, IndexerArgs* ia, TopkArgs* ta,
+                              FusedLayout* layout);
+
 size_t act_row_bytes(const dsa_dims* dims);  // one latent cache row
 size_t idx_row_bytes(const dsa_dims* dims);  // one indexer-key cache row
 

@@ -155,6 +155,34 @@ DSA_API dsa_status dsa_sparse_mla_fwd(const dsa_dims *dims, const void *q, const
                               const int32_t *idx, float *out, float *lse, void *stream);
 
 /*
+ * dsa_indexer_topk -- steps 1 and 2 fused: the top-k selection of the indexer
+ * scores without the score matrix (the feedman.me page's "DSA indexer" row
+ * and its per-query top-2,048 selection).
+ *
+ * Writes idx[n_q][top_k] exactly as dsa_indexer_scores followed by
+ * dsa_topk_select would (same scores, same arithmetic, same tie rule), but
+ * the indexer keeps only each query's candidates: the causal keys scoring at
+ * or above a threshold taken from the query's first 2,048 keys. The select
+ * then runs over those. Queries whose candidates are too few or too many
+ * have their scores computed again (same arithmetic) and are selected from
+ * the full row, so the result never depends on the threshold.
+ *
+ * Arguments as for the two calls, without the score matrix:
+ *   q_idx, w_idx, k_idx_cache   as for dsa_indexer_scores
+ *   idx        [n_q][top_k] int32, as for dsa_topk_select
+ *   workspace  device buffer of ws_bytes >= dsa_indexer_topk_workspace_bytes(dims),
+ *              16-byte aligned; contents on entry do not matter
+ * The fused kernels need bf16 indexer inputs with n_idx_heads == 4, d_idx ==
+ * 128, at most 65,536 cache rows and top_k <= 4,096; for other valid shapes
+ * the call runs the two separate steps with the scores in the workspace.
+ * dsa_indexer_topk_workspace_bytes returns 0 for invalid dims.
+ */
+DSA_API size_t dsa_indexer_topk_workspace_bytes(const dsa_dims *dims);
+DSA_API dsa_status dsa_indexer_topk(const dsa_dims *dims, const void *q_idx, const float *w_idx,
+                                    const void *k_idx_cache, int32_t *idx, void *workspace, size_t ws_bytes,
+                                    void *stream);
+
+/*
  * Decode-shaped attention: steps 3-7 for a chunk of a few queries (1-4 tokens
  * of a decode step, e.g. multi-token drafts), the decode side of the
  * feedman.me page's split (decode runs on the machine holding the cache).

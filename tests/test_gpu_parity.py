@@ -3,7 +3,8 @@
 Every case calls the library through its C ABI (``dsa_top_sparse_amd.binding``)
 on seeded synthetic inputs and compares with ``oracle``:
   * the five workloads C0-C4 on EVERY query row, in blocks of rows: indexer
-    scores and top-k indices bit-exact, attention within max |out - ref| <=
+    scores and top-k indices bit-exact (the indices of both the two-step path
+    and the fused indexer + select), attention within max |out - ref| <=
     4e-3, relative L2 <= 5e-3 (per block, hence over the whole tensor too) and
     |lse - ref| <= 1e-3; the top-k properties also on every row against the
     GPU's scores;
@@ -65,6 +66,14 @@ def gpu_results(torch, name):
         say(f"{name}: top-k properties on every row")
         check_topk_properties(torch, outs["scores"], outs["idx"], cfg.offset, cfg.top_k, name)
         host = {k: outs[k].cpu().numpy() for k in ("scores", "idx", "out", "lse")}
+        say(f"{name}: fused indexer + select")
+        dims = binding.make_dims(cfg)
+        ws = torch.empty(binding.indexer_topk_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+        fidx = torch.full_like(outs["idx"], 12345)
+        binding.indexer_topk(dims, dev["qidx"], dev["w"], dev["kidx"], fidx, ws)
+        torch.cuda.synchronize()
+        host["fused_idx"] = fidx.cpu().numpy()
+        del ws, fidx
         del dev, outs
         torch.cuda.empty_cache()
         _results[name] = (cfg, inputs, host, {"se": 0.0, "sr": 0.0, "max_abs": 0.0, "blocks": 0})
@@ -86,6 +95,8 @@ def test_config_parity(torch_cuda, name, block):
     g_idx = host["idx"][r0:r1]
     bad = np.flatnonzero(np.any(g_idx != ref["idx"], axis=1))
     assert bad.size == 0, f"{name}: indices differ on rows {(bad[:8] + r0).tolist()}"
+    bad = np.flatnonzero(np.any(host["fused_idx"][r0:r1] != ref["idx"], axis=1))
+    assert bad.size == 0, f"{name}: fused indexer + select differs on rows {(bad[:8] + r0).tolist()}"
     check_attention(host["out"][r0:r1], host["lse"][r0:r1], ref["out"], ref["lse"], f"{name} rows {r0}..{r1 - 1}",
                     row_ids=rows)
     max_abs, _, se, sr, _ = attention_errors(host["out"][r0:r1], ref["out"])
