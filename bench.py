@@ -217,20 +217,26 @@ def decode_steps(torch, cfg, dev, stream, reps: int = 20):
     return res
 
 
-def time_workload(torch, binding, cfg, dev, outs, stream, steps, warmup, flush):
+def time_workload(torch, binding, cfg, dev, outs, stream, steps, warmup, flush, fused_ws=None):
     """Per-kernel HIP-event times (ms) of `steps` steps after `warmup` untimed
     ones, on the launch stream. Warm: the steps run back to back in one
     synchronised bracket (wall = that bracket). With `flush`, a buffer is
-    overwritten before every step, outside the events and the wall clock."""
+    overwritten before every step, outside the events and the wall clock.
+    With `fused_ws` (a workspace), steps 1 and 2 are the fused call (timed as
+    'topk', with 'indexer' 0)."""
     dims = binding.make_dims(cfg)
 
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        binding.indexer_scores(dims, dev["qidx"], dev["w"], dev["kidx"], outs["scores"], outs["ld"], stream)
+        if fused_ws is None:
+            binding.indexer_scores(dims, dev["qidx"], dev["w"], dev["kidx"], outs["scores"], outs["ld"], stream)
         if ev:
             ev[1].record(stream)
-        binding.topk_select(dims, outs["scores"], outs["ld"], outs["idx"], outs["workspace"], stream)
+        if fused_ws is None:
+            binding.topk_select(dims, outs["scores"], outs["ld"], outs["idx"], outs["workspace"], stream)
+        else:
+            binding.indexer_topk(dims, dev["qidx"], dev["w"], dev["kidx"], outs["idx"], fused_ws, stream)
         if ev:
             ev[2].record(stream)
         binding.sparse_mla_fwd(dims, dev["q"], dev["kv"], outs["idx"], outs["out"], outs["lse"], stream)
@@ -264,6 +270,24 @@ def time_workload(torch, binding, cfg, dev, outs, stream, steps, warmup, flush):
     return {"wall": wall, "avg": {k: sum(v) / len(v) for k, v in k_ms.items()},
             "med": {k: sorted(v)[len(v) // 2] for k, v in k_ms.items()},
             "min": {k: min(v) for k, v in k_ms.items()}}
+
+
+def path_summary(torch, binding, cfg, dev, outs, stream, two_step, steps=10):
+    """Both ways of running steps 1 and 2 on one workload: the two calls
+    (scores in HBM) and the fused call (candidates only). `two_step` is a
+    time_workload result of the former."""
+    dims = binding.make_dims(cfg)
+    ws = torch.empty(binding.indexer_topk_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    fused = time_workload(torch, binding, cfg, dev, outs, stream, steps, 3, None, fused_ws=ws)
+    del ws
+
+    def ms(t, n):
+        return round(1e3 * t["wall"] / n, 4)
+    return {
+        "two_step": {"ms_per_step": ms(two_step["t"], two_step["steps"]),
+                     "indexer_plus_select_ms": round(two_step["t"]["avg"]["indexer"] + two_step["t"]["avg"]["topk"], 4)},
+        "fused": {"ms_per_step": ms(fused, steps), "indexer_plus_select_ms": round(fused["avg"]["topk"], 4)},
+    }
 
 
 def kernel_summary(cfg, avg):
@@ -344,6 +368,9 @@ def main():
     for k in kernels:
         kernels[k]["median_ms"] = round(med[k], 4)
         kernels[k]["min_ms"] = round(mn[k], 4)
+    paths = None
+    if flush is None and args.replay:
+        paths = path_summary(torch, binding, cfg, dev, outs, stream, {"t": timing, "steps": args.steps})
     if flush is None and args.cold_steps > 0:
         # the HBM-bound steps with L2 and MALL flushed before every step
         big = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -365,7 +392,9 @@ def main():
             t = time_workload(torch, binding, ocfg, odev, oouts, stream, 10, 3, None)
             workloads[ocfg.name] = {"ms_per_step": round(1e3 * t["wall"] / 10, 4),
                                     "query_tokens_per_s": round(ocfg.n_q * 10 / t["wall"], 1),
-                                    "kernels": kernel_summary(ocfg, t["avg"])}
+                                    "kernels": kernel_summary(ocfg, t["avg"]),
+                                    "paths": path_summary(torch, binding, ocfg, odev, oouts, stream,
+                                                          {"t": t, "steps": 10})}
             del odev, oouts
             torch.cuda.empty_cache()
     replay = prefill_replay(torch, cfg, dev, stream) if args.replay else None
@@ -383,6 +412,8 @@ def main():
                    "indexer": f"{cfg.n_idx_heads}x{cfg.d_idx}", "mode": "cold" if args.cold else "warm"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
+    if paths is not None:
+        line["paths"] = paths
     if workloads is not None:
         line["workloads"] = workloads
     if replay is not None:
