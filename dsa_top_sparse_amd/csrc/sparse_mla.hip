@@ -17,7 +17,7 @@
 // form the M = 64 side of both products and no MFMA lane is wasted on
 // masking. Per tile of 32 selected slots:
 //   gather  : all waves issue direct-to-LDS 16-byte loads of the selected
-//             rows, two tiles ahead, into one of 4 key-major LDS stages;
+//             rows, two tiles ahead, into one of 4 LDS stages;
 //   Q K^T   : score waves 0-3 each own 32 heads x 16 slots; S^T = K Q^T on
 //             16x16x32 bf16 MFMAs with the query's Q fragments in registers;
 //   softmax : fp32, exp2 with log2(e) folded into the scale, against a fixed
@@ -142,7 +142,8 @@ constexpr int kThreads = 512;       // 8 waves: 4 score waves + 4 P V waves
 constexpr int kStages = 4;          // LDS tile stages (hi/lo queries use 3; P's lo part takes the 4th)
 constexpr int kRowBytes = kDQK * 2;              // 1152 = 72 pieces of 16 bytes
 constexpr int kStageBytes = kTile * kRowBytes;   // 36 KB
-constexpr int kRingTiles = 24;      // index ring: 3 parts of 8 tiles (1 KB each)
+static_assert(kStageBytes % 256 == 0, "stage bases leave the low 8 address bits alone");
+constexpr int kRingTiles = 32;      // index ring: 4 parts of 8 tiles (1 KB each)
 constexpr int kHiloMaxValid = 512;  // queries with at most this many valid keys use hi/lo P
 constexpr float kRefLog2 = 64.0f;   // P = exp2(s - m_ref) < 2^64 before a restart is forced
 
@@ -171,29 +172,46 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 struct MlaSmem {
   uint8_t stage[kStages][kStageBytes];  // tiles: [32 rows][1 KB latent] then [32 rows][128 B rope]
   uint8_t pbuf[2][kH * kTile * 2];      // P hi part (bf16, chunk-swizzled rows) by tile parity
-  int32_t ring[kRingTiles][kTile];      // the query's index row, tile t at t % 24
+  int32_t ring[kRingTiles][kTile];      // the query's index row, tile t at t % 32
   float hmax[2][kH];                    // [slot half][head]: maxima exchanged between the slot halves
   float lsum[2][kH];                    // [slot half][head]: softmax denominators at the end
   int32_t restart;                      // a head passed its reference by more than kRefLog2
   int32_t c_last, c_valid, c_first;     // index row census
+  int32_t c_firstbad;                   // first tile with a slot that is not a causal key
 };
 
-// A stage holds the 32 rows of a tile as a 1 KB latent part per row (pieces
-// 0..63, 8 dims each) followed by a 128-byte rope part per row (pieces
-// 64..71). The LDS has 64 banks of 4 bytes, i.e. 16 positions of 16 bytes per
-// bank cycle. Latent piece s of row r is stored at s ^ (r & 15) (the XOR stays
-// within aligned groups of 16 pieces); rope piece s of row r at s ^ ((r >> 1) & 7).
-// Both operand reads then spread over all banks: a Q K^T read (one piece of 16
-// consecutive rows) and a transposed P V read (two pieces of 16 rows 8G + e).
-constexpr int kLatBytes = 1024;
-constexpr int kRopeOff = kTile * kLatBytes;  // 32 KB
-__device__ __forceinline__ int swl(int r) { return r & 15; }
+// A stage holds the latent parts of the tile's 32 rows as 4 groups of 8 KB
+// (group g: pieces 16g .. 16g+15, i.e. dims 128g .. 128g+127, of every row, as
+// [32 rows][256 bytes]) followed by the rope parts as [32 rows][128 bytes]
+// (rope pieces 64..71). The LDS has 64 banks of 4 bytes, i.e. 16 positions of
+// 16 bytes per bank cycle, and every row of a group starts a bank cycle.
+// Latent piece 16g + s of row r is stored at position s ^ swl(r) of its row
+// in group g; rope piece s of row r at s ^ ((r >> 1) & 7).
+// swl is the linear map of the row's low four bits b0..b3 that sends b0 to 4,
+// b1 to 8, b2 to 2 and b3 to 3 (XOR-combined). Both operand reads are then
+// free of bank conflicts, as the LDS bank-conflict counter shows for their
+// exact address patterns:
+//  - a Q K^T read (16-byte reads, one piece of 16 consecutive rows per
+//    quarter wave); the plain map swl(r) = r & 15 is conflict-free here too,
+//    but other one-to-one maps, e.g. the bit permutation 2, 4, 1, 8, are not:
+//    the hardware does not serve a 16-byte read as four quarter waves;
+//  - a transposed P V read (8 bytes per lane; pieces 2n, 2n + 1 of rows
+//    8G + 4h + e): swl(r) >> 1 differs for the eight rows (G, e) that one
+//    half wave reads, so the second piece cannot collide. With r & 15, rows
+//    e and e ^ 1 took the same two positions (two-way conflicts).
+// The group-major order lets one 1 KB direct-to-LDS load fill a group of four
+// consecutive rows (64 lanes x 16 bytes land contiguously), so a wave fills
+// its four rows with four loads that differ only in immediate offsets.
+constexpr int kGroupBytes = kTile * 256;      // 8 KB
+constexpr int kRopeOff = 4 * kGroupBytes;     // 32 KB
+__device__ __forceinline__ int swl(int r) { return (((r & 3) << 2) | ((r >> 1) & 2)) ^ (((r >> 3) & 1) * 3); }
 __device__ __forceinline__ int swr(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int lat_off(int r, int s) { return r * kLatBytes + 16 * (s ^ swl(r)); }
+__device__ __forceinline__ int lat_off(int r, int s) { return (s >> 4) * kGroupBytes + r * 256 + 16 * ((s & 15) ^ swl(r)); }
 __device__ __forceinline__ int rope_off(int r, int s) { return kRopeOff + r * 128 + 16 * (s ^ swr(r)); }
 // P rows (one per head, 32 bf16 = 64 bytes = 4 chunks of 8 slots): chunk c of
-// head h is stored at c ^ ((h >> 2) & 3), which keeps both the 8-byte softmax
-// writes and the 16-byte operand reads free of bank conflicts.
+// head h is stored at c ^ ((h >> 2) & 3), which keeps the 16-byte operand
+// reads free of bank conflicts (the two 8-byte softmax writes per tile and
+// score wave still take two-way conflicts, a few cycles per tile).
 __device__ __forceinline__ int p_off(int h, int c) { return h * 64 + 16 * (c ^ ((h >> 2) & 3)); }
 
 // Waits until at most N vector-memory operations of this wave are in flight
@@ -230,66 +248,85 @@ __device__ __forceinline__ s16x4 lds_read_tr(uint32_t a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_u8*)(uintptr_t)a));
 }
 
-// One direct-to-LDS load: 16 bytes per lane from base + off to LDS address
-// lds + 16 * lane. Issued from asm: with the builtin, the compiler cannot tell
+// One direct-to-LDS load: 16 bytes per lane from base + off + IMM to LDS
+// address lds + 16 * lane. The instruction's immediate offset applies to both
+// the global and the LDS address, so M0 is set to lds - IMM. Issued from asm: with the builtin, the compiler cannot tell
 // which LDS reads alias the load and drains every load in flight before the
 // next tile's operand reads. There is no register output to track; M0 is set
 // here and used by nothing else in this kernel; completion is tracked with the
 // explicit vmcnt waits of the tile loop.
+template <int IMM = 0>
 __device__ __forceinline__ void dma16(const void* __restrict__ base, uint32_t off, uint32_t lds) {
+  static_assert(IMM >= 0 && IMM < 4096, "immediate offset range");
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds));
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(off), "s"(base), "i"(IMM), "{m0}"(lds - IMM));
 #pragma clang diagnostic pop
 }
 
-// Byte offset of a selected row in the cache; slots past top_k or holding no
-// valid key load the query's own row instead (always present, finite) and are
-// masked in the softmax, so that every tile costs a fixed number of loads.
-// The offsets are 32-bit (the host checks that the cache is below 4 GiB).
-__device__ __forceinline__ uint32_t row_off(int32_t j, int slot, int top_k, uint32_t p) {
-  return ((slot < top_k && j >= 0 && (uint32_t)j <= p) ? (uint32_t)j : p) * (uint32_t)kRowBytes;
+// Byte offset of a selected row in the cache. A slot holding no causal key
+// (j < 0 or j > p, both above p as unsigned) loads the query's own row
+// instead (always present, finite); so does, possibly, a slot past top_k,
+// whose ring entry is some entry of the row. Such slots are masked in the
+// softmax, so that every tile costs a fixed number of loads. The offsets are
+// 32-bit (the host checks that the cache is below 4 GiB).
+__device__ __forceinline__ uint32_t row_off(int32_t j, uint32_t p) {
+  return min((uint32_t)j, p) * (uint32_t)kRowBytes;
 }
 
 // Tile loads, spread over all 8 waves: wave w loads the latent parts of the
-// rows of slots 4w .. 4w+3 (one 1 KB load each; lane L fills position L of row
-// m, i.e. loads piece L ^ swl(m)), and waves 0-3 also the rope parts of rows
-// 8w .. 8w+7 (one 1 KB load; lane L fills position L % 8 of row 8w + L / 8,
-// i.e. loads rope piece (L % 8) ^ swr(row)). Per tile: 5 loads for waves 0-3,
-// 4 for waves 4-7.
+// rows of slots 4w .. 4w+3, one load per group g (lane L fills position L % 16
+// of row 4w + L / 16 in group g, i.e. loads latent piece 16g + (L % 16) ^
+// swl(row)), and waves 0-3 also the rope parts of rows 8w .. 8w+7 (one load;
+// lane L fills position L % 8 of row 8w + L / 8, i.e. loads rope piece
+// (L % 8) ^ swr(row)). Per tile: 5 loads for waves 0-3, 4 for waves 4-7.
 struct GatherRows {
-  uint32_t lat;   // row offset of slot lane % 32 (taken per load with readlane)
-  uint32_t rope;  // row offset of slot 8w + lane / 8 (waves 0-3)
+  uint32_t lat;   // cache offset of this lane's latent bytes, group 0
+  uint32_t rope;  // cache offset of this lane's rope bytes (waves 0-3)
 };
-__device__ __forceinline__ GatherRows gather_rows(const int32_t* ring_tile, int tile, int wave, int lane, int top_k,
-                                                  uint32_t p) {
-  const int sl = lane & 31, sr = 8 * (wave & 3) + (lane >> 3);
+// Lane constants of the gather: the slot whose row a lane loads and its
+// byte position inside that row's group (latent) or rope part.
+struct GatherLane {
+  int sl, sr;            // latent slot 4w + L / 16, rope slot 8 (w % 4) + L / 8
+  uint32_t lat, rope;    // byte offsets inside the cache row
+};
+__device__ __forceinline__ GatherLane gather_lane(int wave, int lane) {
+  GatherLane gl;
+  gl.sl = 4 * wave + (lane >> 4);
+  gl.sr = 8 * (wave & 3) + (lane >> 3);
+  gl.lat = 16u * (uint32_t)((lane & 15) ^ swl(gl.sl));
+  gl.rope = 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swr(gl.sr));
+  return gl;
+}
+__device__ __forceinline__ GatherRows gather_rows(const int32_t* ring_tile, const GatherLane& gl, uint32_t p) {
   GatherRows g;
-  g.lat = row_off(ring_tile[sl], tile * kTile + sl, top_k, p);
-  g.rope = row_off(ring_tile[sr], tile * kTile + sr, top_k, p);
+  g.lat = row_off(ring_tile[gl.sl], p) + gl.lat;
+  g.rope = row_off(ring_tile[gl.sr], p) + gl.rope;
   return g;
 }
-// Load u of a tile for wave w: u < 4 latent block 4w + u; u = 4 the rope
-// block (waves 0-3 only: the caller knows its role).
+// Load u of a tile for wave w: u < 4 latent group u; u = 4 the rope block
+// (waves 0-3 only: the caller knows its role). u is a constant wherever this
+// is called (unrolled loops), so the switch folds away.
 __device__ __forceinline__ void gather_load(const uint8_t* __restrict__ kv, const GatherRows& g, uint32_t stage_lds,
-                                            uint32_t lane16, uint32_t rope_lane, int u, int wave) {
-  if (u < 4) {
-    const int m = 4 * wave + u;
-    const uint32_t row = __builtin_amdgcn_readlane(g.lat, m);  // wave-uniform
-    dma16(kv + row, lane16 ^ (uint32_t)(16 * (m & 15)), stage_lds + kLatBytes * m);
-  } else {
-    dma16(kv, g.rope + rope_lane, stage_lds + kRopeOff + 1024 * wave);
+                                            int u, int wave) {
+  const uint32_t lds = stage_lds + (uint32_t)(1024 * wave);
+  switch (u) {
+    case 0: dma16<0>(kv, g.lat, lds); break;
+    case 1: dma16<256>(kv, g.lat, lds + kGroupBytes); break;
+    case 2: dma16<512>(kv, g.lat, lds + 2 * kGroupBytes); break;
+    case 3: dma16<768>(kv, g.lat, lds + 3 * kGroupBytes); break;
+    default: dma16(kv, g.rope, lds + kRopeOff); break;
   }
 }
 
 // Index ring refill: tiles 8c .. 8c+7 of the index row (1 KB) into ring part
-// c % 3. Lanes whose 16 bytes would pass the end of the row read the row's
+// c % 4. Lanes whose 16 bytes would pass the end of the row read the row's
 // last 16 bytes instead; their slots lie past top_k and are never used.
 __device__ __forceinline__ void issue_ring(MlaSmem& sm, const int32_t* __restrict__ idx_row, int c, int top_k,
                                            int lane) {
   int s0 = 256 * c + 4 * lane;
   if (s0 + 4 > top_k) s0 = top_k - 4;
-  dma16(idx_row, 4u * (uint32_t)s0, lds_addr(sm.ring[8 * (c % 3)]));
+  dma16(idx_row, 4u * (uint32_t)s0, lds_addr(sm.ring[8 * (c & 3)]));
 }
 
 // One workgroup (8 waves, two per SIMD) per query, in two roles that run side
@@ -300,7 +337,11 @@ __device__ __forceinline__ void issue_ring(MlaSmem& sm, const int32_t* __restric
 //     softmax of those scores; P goes to LDS as bf16;
 //   P V waves (w = 4..7; v = w - 4): O += P V for output dims 128 v .. +127
 //     of all 64 heads.
-// All waves share the direct-to-LDS tile loads, issued between their MFMAs.
+// All waves share the direct-to-LDS tile loads, which each wave issues right
+// after the barrier, before its products: the earlier they leave, the more of
+// the gather latency the tile in between covers (issuing them between the
+// products instead left the score waves waiting about 500 cycles per tile for
+// their last rows).
 // In iteration t the score waves work on tile t and the P V waves on tile
 // t - 1, while tiles t + 1 and t + 2 are loading (4 stages).
 //
@@ -334,16 +375,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   const int l16 = lane & 15, q4 = lane >> 4;
   const int32_t* __restrict__ idx_row = idx + (int64_t)i * row_slots + (int64_t)split * split_slots;
   const uint8_t* __restrict__ kvb = reinterpret_cast<const uint8_t*>(kv);
-  const uint32_t stage0_lds = lds_addr(sm.stage[0]);
-  const uint32_t pbuf_lds = lds_addr(sm.pbuf[0]);
-  const uint32_t plo_lds = lds_addr(sm.stage[kStages - 1]);  // P lo parts (hi/lo queries)
+  uint32_t stage0_lds = lds_addr(sm.stage[0]);
+  uint32_t pbuf_lds = lds_addr(sm.pbuf[0]);
+  uint32_t plo_lds = lds_addr(sm.stage[kStages - 1]);  // P lo parts (hi/lo queries)
+  // Held in scalar registers from here on (otherwise the compiler recomputes
+  // the address-space conversions inside the tile loops).
+  asm volatile("" : "+s"(stage0_lds), "+s"(pbuf_lds), "+s"(plo_lds));
   const uint32_t lane16 = 16u * (uint32_t)lane;
-  const uint32_t rope_lane = 2u * kDL + 16u * (uint32_t)((lane & 7) ^ swr(8 * (wave & 3) + (lane >> 3)));
+  const GatherLane gl = gather_lane(wave, lane);
 
   if (tid == 0) {
     sm.c_last = 0;
     sm.c_valid = 0;
     sm.c_first = 0x7fffffff;
+    sm.c_firstbad = (top_k % kTile) ? top_k / kTile : 0x7fffffff;  // a partial last tile is masked
     sm.restart = 0;
   }
   __syncthreads();
@@ -351,10 +396,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   // Census of the index row (valid slots, last valid slot, first tile with a
   // valid slot), then the tile range. Called by both roles after they have
   // issued their own first loads, so that the latencies overlap.
-  int n_tiles = 0, first_tile = 0, t0 = 0;
+  int n_tiles = 0, first_tile = 0, t0 = 0, first_bad = 0;
   bool hilo = false;
   auto census = [&]() {
-    int last = 0, cnt = 0, first = 0x7fffffff;
+    int last = 0, cnt = 0, first = 0x7fffffff, bad = 0x7fffffff;
     for (int b = 4 * tid; b < top_k; b += 4 * kThreads) {  // top_k % 4 == 0: 16-byte reads
       const u32x4 j4 = *reinterpret_cast<const u32x4*>(idx_row + b);
 #pragma unroll
@@ -363,16 +408,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
           last = b + r + 1;
           first = min(first, (b + r) / kTile);
           ++cnt;
+        } else {
+          bad = min(bad, (b + r) / kTile);
         }
       }
     }
     last = wave_max_int(last);
     cnt = wave_sum_int(cnt);
     first = wave_min_int(first);
+    bad = wave_min_int(bad);
     if (lane == 0) {
       atomicMax(&sm.c_last, last);
       atomicAdd(&sm.c_valid, cnt);
       atomicMin(&sm.c_first, first);
+      atomicMin(&sm.c_firstbad, bad);
     }
     if (wave == 7) {  // index ring, tiles 0..15 (reloaded below if the first valid tile lies further)
       issue_ring(sm, idx_row, 0, top_k, lane);
@@ -386,6 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     __syncthreads();
     n_tiles = (sm.c_last + kTile - 1) / kTile;
     first_tile = n_tiles > 0 ? sm.c_first : 0;
+    first_bad = sm.c_firstbad;
     t0 = first_tile & ~7;  // the loop starts at a ring chunk boundary
     hilo = sm.c_valid <= kHiloMaxValid;
     if (t0 != 0) {  // rare: no valid slot in tiles 0..7
@@ -399,37 +449,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
   };
 
   // Waits, before the barrier of iteration t, for this wave's loads of tile
-  // t: the loads of tile t + 1 and a ring refill issued in iteration t - 1
-  // (wave 7) may stay in flight.
-  auto wait_tile = [&](int t, auto hilo_c) {
+  // t: only the loads of tile t + 1, the last ones this wave issued, may stay
+  // in flight (a ring refill, issued before them, completes here too).
+  // STEADY: t + 1 < n_tiles is known.
+  auto wait_tile = [&](int t, auto hilo_c, auto steady_c) {
     constexpr bool HILO = decltype(hilo_c)::value;
-    if (t >= n_tiles) return;
-    if (HILO) {  // tile t + 1 is issued after this barrier
+    constexpr bool STEADY = decltype(steady_c)::value;
+    if (!STEADY && t >= n_tiles) return;
+    if (HILO || (!STEADY && t + 1 >= n_tiles)) {  // HILO: tile t + 1 is issued after this barrier
       wait_vmcnt<0>();
-      return;
-    }
-    const bool next_out = t + 1 < n_tiles;
-    const bool ring_out = wave == 7 && ((t - 1) & 7) == 0 && t - 1 >= t0 + 8 && 8 * ((t - 1) / 8 + 1) < n_tiles;
-    if (wave < 4) {
-      if (next_out) wait_vmcnt<5>();
-      else wait_vmcnt<0>();
-    } else if (next_out) {
-      if (ring_out) wait_vmcnt<5>();
-      else wait_vmcnt<4>();
+    } else if (wave < 4) {
+      wait_vmcnt<5>();
     } else {
-      if (ring_out) wait_vmcnt<1>();
-      else wait_vmcnt<0>();
+      wait_vmcnt<4>();
     }
   };
   auto issue_all = [&](const GatherRows& g, uint32_t stage_lds) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) gather_load(kvb, g, stage_lds, lane16, rope_lane, u, wave);
-    if (wave < 4) gather_load(kvb, g, stage_lds, lane16, rope_lane, 4, wave);
+    for (int u = 0; u < 4; ++u) gather_load(kvb, g, stage_lds, u, wave);
+    if (wave < 4) gather_load(kvb, g, stage_lds, 4, wave);
   };
   auto start_pipeline = [&](int ahead) {
     for (int a = 0; a < ahead; ++a)
       if (t0 + a < n_tiles)
-        issue_all(gather_rows(sm.ring[(t0 + a) % kRingTiles], t0 + a, wave, lane, top_k, p32),
+        issue_all(gather_rows(sm.ring[(t0 + a) & (kRingTiles - 1)], gl, p32),
                   stage0_lds + kStageBytes * a);
   };
 
@@ -443,8 +486,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) head[hb] = 32 * g + 16 * hb + l16;
     // K operand (A): row 16 s + l16 of the tile, piece 4u + q4. For u < 16 the
-    // swizzle keeps the piece inside its group of 16, so the offset is
-    // qk_lat[u % 4] + 256 (u / 4); the rope k-steps u = 16, 17 have their own.
+    // piece lies in group u / 4, so the offset is qk_lat[u % 4] + 8 KB (u / 4);
+    // the rope k-steps u = 16, 17 have their own.
     const int krow = 16 * s + l16;
     uint32_t qk_lat[4], qk_rope[2];
 #pragma unroll
@@ -470,92 +513,107 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     // latency sits between the barrier and the first operand reads.
     auto ring_rows = [&](int t) {
       const int tn = t + kAhead;
-      return gather_rows(sm.ring[(tn < n_tiles ? tn : t0) % kRingTiles], tn, wave, lane, top_k, p32);
+      return gather_rows(sm.ring[(tn < n_tiles ? tn : t0) & (kRingTiles - 1)], gl, p32);
     };
-    auto ring_slots = [&](int t) { return *reinterpret_cast<const u32x4*>(&sm.ring[t % kRingTiles][16 * s + 4 * q4]); };
+    auto ring_slots = [&](int t) {
+      return *reinterpret_cast<const u32x4*>(&sm.ring[t & (kRingTiles - 1)][16 * s + 4 * q4]);
+    };
     auto pass = [&](const bf16x8 (&qf)[2][18], bool first_pass) {
       start_pipeline(kAhead);
       int st = 0;  // stage of tile t
       GatherRows rows = ring_rows(t0);
       u32x4 jv = ring_slots(t0);
-      for (int t = t0; t <= n_tiles; ++t) {
-        wait_tile(t, hilo_c);
+      // One iteration; STEADY: first_tile < t and t + kAhead < n_tiles.
+      auto body = [&](int t, auto steady_c) {
+        constexpr bool STEADY = decltype(steady_c)::value;
+        wait_tile(t, hilo_c, steady_c);
         lds_barrier();  // B(t): tile t resident; P(t - 1) complete
-        const int t_next = t + kAhead;
-        const bool more = t_next < n_tiles;
+        const bool more = STEADY || t + kAhead < n_tiles;
         int sn = st + kAhead;
         if (sn >= S) sn -= S;
         const uint32_t next_lds = stage0_lds + kStageBytes * sn;
         GatherRows rows_n;
         u32x4 jv_n;
-        if (t < n_tiles && t >= first_tile) {
-          // ---- S^T = K Q^T; tile t + kAhead's loads go out between the MFMAs
+        if (STEADY || (t < n_tiles && t >= first_tile)) {
+          // ---- tile t + kAhead's loads, then S^T = K Q^T
+          if (more) issue_all(rows, next_lds);
           const uint32_t tile_lds = stage0_lds + kStageBytes * st;
           uint32_t kb[6];
 #pragma unroll
           for (int x = 0; x < 4; ++x) kb[x] = tile_lds + qk_lat[x];
 #pragma unroll
           for (int x = 0; x < 2; ++x) kb[4 + x] = tile_lds + qk_rope[x];
-          // The operand reads run three k-steps ahead (written out, since the
-          // load branches split the sequence into blocks the scheduler cannot
-          // move reads across).
+          // The operand reads run six k-steps ahead.
           auto kread = [&](int u) {
-            return __builtin_bit_cast(bf16x8, lds_read16((u < 16) ? kb[u & 3] + 256 * (u >> 2) : kb[4 + (u - 16)]));
+            return __builtin_bit_cast(bf16x8,
+                                      lds_read16((u < 16) ? kb[u & 3] + kGroupBytes * (u >> 2) : kb[4 + (u - 16)]));
           };
           f32x4 sacc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-          bf16x8 kf[3] = {kread(0), kread(1), kread(2)};
+          constexpr int kLead = 6;
+          bf16x8 kf[kLead];
+#pragma unroll
+          for (int x = 0; x < kLead; ++x) kf[x] = kread(x);
 #pragma unroll
           for (int u = 0; u < 18; ++u) {
-            const bf16x8 cur = kf[u % 3];
-            if (u + 3 < 18) kf[u % 3] = kread(u + 3);
+            const bf16x8 cur = kf[u % kLead];
+            if (u + kLead < 18) kf[u % kLead] = kread(u + kLead);
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb)
               sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qf[hb][u], sacc[hb], 0, 0, 0);
-            if (more && u % 3 == 1 && u / 3 < 5) gather_load(kvb, rows, next_lds, lane16, rope_lane, u / 3, wave);
           }
           rows_n = ring_rows(t + 1);
-          jv_n = ring_slots(t + 1);
-          // ---- slot validity (from the ring)
-          const int gs0 = t * kTile + 16 * s + 4 * q4;
-          bool vm[4];
+          jv_n = jv;
+          if (t + 1 >= first_bad) jv_n = ring_slots(t + 1);
+          // ---- slot validity and softmax numerators. Tiles before the first
+          // one holding a non-causal slot (every tile, for an index row that
+          // lists causal keys and then pads) need no masks.
+          auto softmax = [&](auto masked_c) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            bool vm[4] = {true, true, true, true};
+            if (MASKED) {
+              const int gs0 = t * kTile + 16 * s + 4 * q4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) vm[r] = gs0 + r < top_k && jv[r] <= p32;
-          if (first_pass && t == first_tile) {  // reference: the head's max over this tile
+              for (int r = 0; r < 4; ++r) vm[r] = gs0 + r < top_k && jv[r] <= p32;
+            }
+            if (!STEADY && first_pass && t == first_tile) {  // reference: the head's max over this tile
+#pragma unroll
+              for (int hb = 0; hb < 2; ++hb) {
+                float lm = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (vm[r]) lm = fmaxf(lm, scaled(sacc[hb][r]));
+                const float hm = max_over_q4(lm);
+                if (q4 == 0) sm.hmax[s][head[hb]] = hm;
+              }
+              lds_barrier();  // X: both slot halves' maxima published
+#pragma unroll
+              for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(sm.hmax[0][head[hb]], sm.hmax[1][head[hb]]);
+            }
+            // P = exp2(s * scale - m_ref), bf16 to LDS (the product is rounded
+            // as in the reference, so its maximum gets P = 1 exactly)
+            const uint32_t par = (uint32_t)(t & 1) * (kH * kTile * 2);
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
-              float lm = -INFINITY;
+              float x[4];
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (vm[r]) lm = fmaxf(lm, scaled(sacc[hb][r]));
-              const float hm = max_over_q4(lm);
-              if (q4 == 0) sm.hmax[s][head[hb]] = hm;
+              for (int r = 0; r < 4; ++r) x[r] = (!MASKED || vm[r]) ? scaled(sacc[hb][r]) - m_ref[hb] : -INFINITY;
+              runmax[hb] = fmaxf(runmax[hb], fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+              float pv[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(x[r]);
+              l_part[hb] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+              const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
+              const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
+              lds_write8(pbuf_lds + par + poff[hb], u32x2{h0, h1});
+              if (HILO) {
+                const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
+                const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
+                lds_write8(plo_lds + par + poff[hb], u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)});
+              }
             }
-            lds_barrier();  // X: both slot halves' maxima published
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) m_ref[hb] = fmaxf(sm.hmax[0][head[hb]], sm.hmax[1][head[hb]]);
-          }
-          // ---- softmax numerators P = exp2(s * scale - m_ref), bf16 to LDS (the
-          // product is rounded as in the reference, so its maximum gets P = 1 exactly)
-          const uint32_t par = (uint32_t)(t & 1) * (kH * kTile * 2);
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            float x[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = vm[r] ? scaled(sacc[hb][r]) - m_ref[hb] : -INFINITY;
-            runmax[hb] = fmaxf(runmax[hb], fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-            float pv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(x[r]);
-            l_part[hb] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-            const uint32_t h0 = cvt_pk_bf16(pv[0], pv[1]);
-            const uint32_t h1 = cvt_pk_bf16(pv[2], pv[3]);
-            lds_write8(pbuf_lds + par + poff[hb], u32x2{h0, h1});
-            if (HILO) {
-              const float r0 = pv[0] - __uint_as_float(h0 << 16), r1 = pv[1] - __uint_as_float(h0 & 0xFFFF0000u);
-              const float r2 = pv[2] - __uint_as_float(h1 << 16), r3 = pv[3] - __uint_as_float(h1 & 0xFFFF0000u);
-              lds_write8(plo_lds + par + poff[hb], u32x2{cvt_pk_bf16(r0, r1), cvt_pk_bf16(r2, r3)});
-            }
-          }
+          };
+          if (t >= first_bad) softmax(std::true_type{});
+          else softmax(std::false_type{});
         } else {
           if (more) issue_all(rows, next_lds);
           rows_n = ring_rows(t + 1);
@@ -564,6 +622,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
         rows = rows_n;
         jv = jv_n;
         st = (st + 1 == S) ? 0 : st + 1;
+      };
+      for (int t = t0; t <= n_tiles; ++t) {
+        if (t > first_tile && t + kAhead < n_tiles) body(t, std::true_type{});
+        else body(t, std::false_type{});
       }
     };
 
@@ -610,12 +672,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
     const int v = wave - 4;
     // Transposed V reads (B operand): lane 16G + 4e + c addresses row
     // 8G + 4h + e, dims 128v + 16nb + 4c .. +3 (piece 16v + 2nb + c/2, byte
-    // 8 (c % 2) inside it); entry x = 2 nb + h.
-    uint32_t tr_base[16];
+    // 8 (c % 2) inside it). The piece's position is 2nb ^ ((c / 2) ^ swl(row)),
+    // so the address for dim block nb is tr_base[h] ^ 32 nb (the stage base,
+    // a multiple of 256, does not touch those bits).
+    uint32_t tr_base[2];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int nb = x >> 1, h = x & 1, e = l16 >> 2, c = l16 & 3;
-      tr_base[x] = lat_off(8 * q4 + 4 * h + e, 16 * v + 2 * nb + (c >> 1)) + 8 * (c & 1);
+    for (int h = 0; h < 2; ++h) {
+      const int e = l16 >> 2, c = l16 & 3;
+      tr_base[h] = lat_off(8 * q4 + 4 * h + e, 16 * v + (c >> 1)) + 8 * (c & 1);
     }
     // P operand (A): head 16 mb + l16, slots 8 q4 .. +7; the head block adds 1 KB.
     const uint32_t pr = (uint32_t)p_off(l16, q4);
@@ -627,31 +691,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 
     auto ring_rows = [&](int t) {  // read one iteration ahead, as in the score waves
       const int tn = t + kAhead;
-      return gather_rows(sm.ring[(tn < n_tiles ? tn : t0) % kRingTiles], tn, wave, lane, top_k, p32);
+      return gather_rows(sm.ring[(tn < n_tiles ? tn : t0) & (kRingTiles - 1)], gl, p32);
     };
     auto pass = [&](bool first_pass) {
       start_pipeline(kAhead);
       int st = 0;  // stage of tile t
       GatherRows rows = ring_rows(t0);
+      // (One loop body: two specialised copies, as in the score waves, would
+      // each need their own registers for the 128 accumulators.)
       for (int t = t0; t <= n_tiles; ++t) {
-        wait_tile(t, hilo_c);
+        wait_tile(t, hilo_c, std::false_type{});
         lds_barrier();  // B(t)
         if (wave == 7 && (t & 7) == 0 && t >= t0 + 8 && 8 * (t / 8 + 1) < n_tiles)
           issue_ring(sm, idx_row, t / 8 + 1, top_k, lane);
-        const int t_next = t + kAhead;
-        const bool more = t_next < n_tiles;
+        const bool more = t + kAhead < n_tiles;
         int sn = st + kAhead;
         if (sn >= S) sn -= S;
         const uint32_t next_lds = stage0_lds + kStageBytes * sn;
         GatherRows rows_n;
         if (t - 1 >= first_tile) {
-          // ---- O += P V for tile t - 1; tile t + kAhead's loads go out between the MFMAs
+          // ---- tile t + kAhead's loads, then O += P V for tile t - 1
+          if (more) issue_all(rows, next_lds);
           const uint32_t tile_lds = stage0_lds + kStageBytes * (st == 0 ? S - 1 : st - 1);
           const uint32_t par = (uint32_t)((t - 1) & 1) * (kH * kTile * 2);
-          // V operand reads run two dim blocks ahead (see the score waves).
+          // V operand reads run two dim blocks ahead.
           auto vread = [&](int nb) {
-            const s16x4 d0 = lds_read_tr(tile_lds + tr_base[2 * nb]);
-            const s16x4 d1 = lds_read_tr(tile_lds + tr_base[2 * nb + 1]);
+            const s16x4 d0 = lds_read_tr((tile_lds + tr_base[0]) ^ (uint32_t)(32 * nb));
+            const s16x4 d1 = lds_read_tr((tile_lds + tr_base[1]) ^ (uint32_t)(32 * nb));
             return __builtin_bit_cast(bf16x8, (s16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]}));
           };
 #pragma unroll
@@ -668,8 +734,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 #pragma unroll
               for (int mb = 0; mb < 4; ++mb)
                 o[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mb], cur, o[mb][nb], 0, 0, 0);
-              if (more && part == 0 && (nb & 1) == 0) gather_load(kvb, rows, next_lds, lane16, rope_lane, nb >> 1, wave);
               if (part == 0 && nb == 5) rows_n = ring_rows(t + 1);
+              // keep the reads two dim blocks ahead, not all at the top (registers)
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
         } else {
