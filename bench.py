@@ -58,15 +58,16 @@ def kernel_source_sha(name: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel_file: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counters, if they match the current source."""
+def measured_traffic(kernel: str, kernel_file: str, workload: str):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counters, if
+    they were taken on the current source of its file."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    r = rec.get(workload, {}).get(kernel_file)
-    if not r or r.get("source_sha") != kernel_source_sha(kernel_file):
+    r = rec.get(workload, {}).get(kernel)
+    if not r or r.get("source") != kernel_file or r.get("source_sha") != kernel_source_sha(kernel_file):
         return None
     return r.get("bytes_per_launch")
 
@@ -290,10 +291,18 @@ def path_summary(torch, binding, cfg, dev, outs, stream, two_step, steps=10):
     }
 
 
-def kernel_summary(cfg, avg):
-    """Per-kernel time and fraction of its roofline from average launch times (ms)."""
+def kernel_summary(cfg, avg, fused=False):
+    """Per-kernel time and fraction of its roofline from average launch times (ms).
+    fused: steps 1 and 2 ran as the fused call (its time is avg["topk"])."""
     w_idx, w_topk, w_attn = algorithmic_work(cfg)
     t_attn = avg["attention"] * 1e-3
+    if fused:
+        return {
+            "indexer_topk_fused": {"ms": round(avg["topk"], 4)},
+            "attention": {"ms": round(avg["attention"], 4), "bound": "mfma",
+                          "mfma_frac": round(w_attn["flops"] / t_attn / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "gather_GBs": round(w_attn["gathered_bytes"] / t_attn / 1e9, 1)},
+        }
     return {
         "indexer": {"ms": round(avg["indexer"], 4), "bound": "hbm",
                     "hbm_frac": round(w_idx["bytes"] / (avg["indexer"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -319,6 +328,9 @@ def main():
     ap.add_argument("--no-replay", dest="replay", action="store_false",
                     help="skip the side measurements: the other workloads, chunked-prefill replays of the pages' "
                          "prompts, and decode steps")
+    ap.add_argument("--path", choices=("two_step", "fused"), default="two_step",
+                    help="steps 1-2 as two calls (scores in HBM; the faster one on the 8k chunk at offset 8k) or as "
+                         "the fused indexer + select")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference kernel for the HBM byte counters)")
     args = ap.parse_args()
@@ -351,7 +363,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    timing = time_workload(torch, binding, cfg, dev, outs, stream, args.steps, args.warmup, flush)
+    fused_ws = None
+    if args.path == "fused":
+        fused_ws = torch.empty(binding.indexer_topk_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    timing = time_workload(torch, binding, cfg, dev, outs, stream, args.steps, args.warmup, flush, fused_ws=fused_ws)
     wall = timing["wall"]
     avg, med, mn = timing["avg"], timing["med"], timing["min"]
     ms_per_step = 1e3 * wall / args.steps
@@ -359,19 +374,21 @@ def main():
     w_idx, w_topk, w_attn = algorithmic_work(cfg)
     t_attn = avg["attention"] * 1e-3
     attn_tflops = w_attn["flops"] / t_attn / 1e12
-    traffic = measured_traffic("sparse_mla.hip", cfg.name)
+    traffic = measured_traffic("mla_mfma_kernel", "sparse_mla.hip", cfg.name)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "mla_mfma_kernel", "flops_per_launch": w_attn["flops"],
                 "avg_launch_ms": round(avg["attention"], 4)}
-    kernels = kernel_summary(cfg, avg)
-    for k in kernels:
-        kernels[k]["median_ms"] = round(med[k], 4)
-        kernels[k]["min_ms"] = round(mn[k], 4)
+    fused = fused_ws is not None
+    kernels = kernel_summary(cfg, avg, fused)
+    for k, src in (("indexer", "indexer"), ("topk", "topk"), ("indexer_topk_fused", "topk"), ("attention", "attention")):
+        if k in kernels:
+            kernels[k]["median_ms"] = round(med[src], 4)
+            kernels[k]["min_ms"] = round(mn[src], 4)
     paths = None
-    if flush is None and args.replay:
+    if flush is None and args.replay and not fused:
         paths = path_summary(torch, binding, cfg, dev, outs, stream, {"t": timing, "steps": args.steps})
-    if flush is None and args.cold_steps > 0:
+    if flush is None and args.cold_steps > 0 and not fused:
         # the HBM-bound steps with L2 and MALL flushed before every step
         big = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         cold = time_workload(torch, binding, cfg, dev, outs, stream, args.cold_steps, 0, big)
@@ -409,7 +426,8 @@ def main():
         "data": "synthetic (seeded; shapes of the pages' 2k/8k-chunk prefill workloads)",
         "config": {"workload": cfg.name, "chunk": cfg.n_q, "offset": cfg.offset, "context": cfg.t_ctx,
                    "heads": cfg.n_heads, "d_qk": cfg.d_qk, "d_v": cfg.d_latent, "top_k": cfg.top_k,
-                   "indexer": f"{cfg.n_idx_heads}x{cfg.d_idx}", "mode": "cold" if args.cold else "warm"},
+                   "indexer": f"{cfg.n_idx_heads}x{cfg.d_idx}", "mode": "cold" if args.cold else "warm",
+                   "path": args.path},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     if paths is not None:

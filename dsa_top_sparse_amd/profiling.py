@@ -31,10 +31,16 @@ CSRC = os.path.join(ROOT, "dsa_top_sparse_amd", "csrc")
 # kernel symbol fragment -> (source file, short name)
 KERNELS = {
     "mla_mfma_kernel": ("sparse_mla.hip", "mla_mfma_kernel"),
-    "indexer_mfma_kernel": ("indexer.hip", "indexer_mfma_kernel"),
+    "mla_combine_kernel": ("sparse_mla.hip", "mla_combine_kernel"),
+    "mla_plain_kernel": ("sparse_mla.hip", "mla_plain_kernel"),
+    "indexer_lds_kernel<true>": ("indexer.hip", "indexer_lds_kernel<true>"),
     "indexer_lds_kernel": ("indexer.hip", "indexer_lds_kernel"),
-    "topk_reg_kernel": ("topk.hip", "topk_reg_kernel"),
+    "indexer_mfma_kernel": ("indexer.hip", "indexer_mfma_kernel"),
+    "indexer_plain_kernel": ("indexer.hip", "indexer_plain_kernel"),
+    "topk_filter_kernel": ("topk.hip", "topk_filter_kernel"),
     "topk_kernel": ("topk.hip", "topk_kernel"),
+    "tau_kernel": ("fused.hip", "tau_kernel"),
+    "cand_select_kernel": ("fused.hip", "cand_select_kernel"),
 }
 COPY_KERNEL = "copyBuffer"
 COPY_BYTES = float(1 << 30)  # bench.py --copy-calibration: 2^28 fp32 read and written
@@ -98,7 +104,9 @@ def read_counter(pmc_dir: str, counter: str):
             per.setdefault(k[1], []).append(v)
     if not copy:
         raise RuntimeError(f"no copy-kernel dispatch in {pmc_dir}: run bench.py with --copy-calibration")
-    return {k: statistics.mean(v) for k, v in per.items()}, statistics.mean(copy)
+    # the calibration copy is the largest one; other, small device copies of
+    # the run (argument and workspace set-up) are not it
+    return {k: statistics.mean(v) for k, v in per.items()}, max(copy)
 
 
 def main():
@@ -144,8 +152,8 @@ def main():
         sha = source_sha(src)
         lines.append(f"| {short} | {st['calls']} | {st['avg_us']:.1f} | {st['timed_avg_us']:.1f} | {st['min_us']:.1f} | {st['max_us']:.1f} | "
                      f"{st['pct']:.1f}% | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {sha} |")
-        traffic.setdefault(args.workload, {})[src] = {
-            "kernel": short, "bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+        traffic.setdefault(args.workload, {})[short] = {
+            "source": src, "bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
             "fetch_scale": f_fetch, "write_scale": f_write, "avg_launch_us": st["timed_avg_us"], "source_sha": sha}
     with open(os.path.join(args.out, f"kernels_{args.workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
