@@ -261,9 +261,17 @@ def sparse_mla_decode_noalloc(dims: Dims, q, kv, idx, out, lse=None, stream=None
 
 def prefill_chunk(dims: Dims, q, kv_chunk, q_idx, w_idx, k_idx_chunk, kv_cache, k_idx_cache, scores, ld: int,
                   idx, out, lse=None, workspace=None, stream=None) -> None:
+    """scores=None runs steps 1-2 fused (dsa_indexer_topk); workspace must then
+    hold indexer_topk_workspace_bytes(dims) bytes."""
     _contig(q, kv_chunk, q_idx, w_idx, k_idx_chunk, kv_cache, k_idx_cache, scores, idx, out, lse)
-    _check_indexer_sizes(dims, q_idx, w_idx, k_idx_cache, scores, ld)
-    _check_topk_sizes(dims, scores, ld, idx)
+    if scores is None:
+        ld = 0
+        need = indexer_topk_workspace_bytes(dims)
+        if dims.n_q > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            raise ValueError(f"dsa_prefill_chunk without scores needs a workspace of {need} bytes")
+    else:
+        _check_indexer_sizes(dims, q_idx, w_idx, k_idx_cache, scores, ld)
+        _check_topk_sizes(dims, scores, ld, idx)
     _check_mla_sizes(dims, q, kv_cache, idx, out, lse)
     if dims.n_q > 0:
         _fits(kv_chunk, dims.n_q * (dims.d_latent + dims.d_rope), _act_size(dims), "kv_chunk")

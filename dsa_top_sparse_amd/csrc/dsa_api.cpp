@@ -132,17 +132,20 @@ dsa_status dsa_prefill_chunk(const dsa_dims* dims, const void* q, const void* kv
                              const float* w_idx, const void* k_idx_chunk, void* kv_cache, void* k_idx_cache,
                              float* scores, int64_t ld, int32_t* idx, float* out, float* lse, void* workspace,
                              size_t ws_bytes, void* stream) {
-  (void)workspace;
   dsa::IndexerArgs ia{};
   dsa::TopkArgs ta{};
   dsa::MlaArgs ma{};
-  dsa_status st = dsa::check_indexer(dims, q_idx, w_idx, k_idx_cache, scores, ld, &ia);
-  if (st == DSA_OK) st = dsa::check_topk(dims, scores, ld, idx, ws_bytes, &ta);
+  dsa::FusedLayout L{};
+  const bool fused = scores == nullptr;  // steps 1-2 as dsa_indexer_topk
+  dsa_status st = fused ? dsa::check_indexer_topk(dims, q_idx, w_idx, k_idx_cache, idx, workspace, ws_bytes, &ia,
+                                                   &ta, &L)
+                        : dsa::check_indexer(dims, q_idx, w_idx, k_idx_cache, scores, ld, &ia);
+  if (st == DSA_OK && !fused) st = dsa::check_topk(dims, scores, ld, idx, ws_bytes, &ta);
   if (st == DSA_OK) st = dsa::check_mla(dims, q, kv_cache, idx, out, lse, &ma);
   if (st != DSA_OK || dims->n_q == 0) return st;
   if ((st = dsa::check_append(dims, kv_chunk, k_idx_chunk, kv_cache, k_idx_cache)) != DSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = ready(kIndexer | kTopk | kMla, s)) != DSA_OK) return st;
+  if ((st = ready(kIndexer | kTopk | kMla | (fused && L.fused ? kFused : 0), s)) != DSA_OK) return st;
   const size_t kv_row = dsa::act_row_bytes(dims), kx_row = dsa::idx_row_bytes(dims);
   uint8_t* kv_dst = static_cast<uint8_t*>(kv_cache) + kv_row * (size_t)dims->offset;
   uint8_t* kx_dst = static_cast<uint8_t*>(k_idx_cache) + kx_row * (size_t)dims->offset;
@@ -153,8 +156,12 @@ dsa_status dsa_prefill_chunk(const dsa_dims* dims, const void* q, const void* kv
   if (k_idx_chunk != kx_dst &&
       hipMemcpyAsync(kx_dst, k_idx_chunk, kx_row * (size_t)dims->n_q, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return DSA_ERR_DEVICE;
-  if ((st = from_hip(dsa::launch_indexer(ia, s))) != DSA_OK) return st;
-  if ((st = from_hip(dsa::launch_topk(ta, s))) != DSA_OK) return st;
+  if (fused) {
+    if ((st = from_hip(dsa::launch_indexer_topk(ia, ta, L, workspace, s))) != DSA_OK) return st;
+  } else {
+    if ((st = from_hip(dsa::launch_indexer(ia, s))) != DSA_OK) return st;
+    if ((st = from_hip(dsa::launch_topk(ta, s))) != DSA_OK) return st;
+  }
   return from_hip(dsa::launch_mla(ma, s));
 }
 

@@ -245,6 +245,14 @@ DSA_API dsa_status dsa_sparse_mla_decode_noalloc(const dsa_dims *dims, const voi
  *   kv_chunk, k_idx_chunk  the chunk's new cache rows (device, 16-byte aligned;
  *                          must not partially overlap their destination)
  *   kv_cache, k_idx_cache  caches with room for offset + n_q rows
+ *   scores     as for dsa_indexer_scores, or NULL: steps 1 and 2 then run as
+ *              dsa_indexer_topk (same indices, no score matrix; `ld` is
+ *              ignored) with `workspace` of ws_bytes >=
+ *              dsa_indexer_topk_workspace_bytes(dims). On MI355X that is the
+ *              faster way once the context reaches about 32k keys; below it
+ *              the two calls are as fast or faster.
+ *   workspace, ws_bytes  as for dsa_topk_select (which needs none), or the
+ *              fused call's workspace when scores is NULL
  * Every argument of the three steps is validated before anything is enqueued.
  */
 DSA_API dsa_status dsa_prefill_chunk(const dsa_dims *dims, const void *q, const void *kv_chunk,

@@ -133,7 +133,8 @@ def test_prefill_chunk_rejects_bad_arguments(L):
     assert call(dims(sm_scale=float("nan"))) == SHAPE
     assert call(dims(), kv_chunk=None) == NULL
     assert call(dims(), kx_chunk=FAKE + 4) == ALIGN
-    assert call(dims(), scores=None) == NULL
+    # no score matrix: steps 1-2 run fused and need the fused call's workspace
+    assert call(dims(), scores=None) == WS
     # a chunk that partially overlaps its destination rows
     d = dims()
     dst = FAKE * 2 + d.offset * 1152

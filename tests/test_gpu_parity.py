@@ -479,8 +479,9 @@ def test_chunked_prefill_replay(torch_cuda):
 
 def test_prefill_replay_17k_prompt_2k_chunks(torch_cuda):
     # The pages' 17.5k-token prompt (17,536 tokens) from empty caches in
-    # 2,048-token chunks (nine calls, the last of 1,152 tokens) and in
-    # 8,192-token chunks, against the whole prompt as one chunk: index sets,
+    # 2,048-token chunks (nine calls, the last of 1,152 tokens; once more with
+    # the indexer and select fused) and in 8,192-token chunks, against the
+    # whole prompt as one chunk: index sets,
     # outputs and lse bit-identical; rows on both sides of every chunk edge
     # against the oracle.
     from dsa_top_sparse_amd import prefill
@@ -498,7 +499,13 @@ def test_prefill_replay_17k_prompt_2k_chunks(torch_cuda):
         prefill.run_prefill(cfg, dev, chunk, o, scores=scores)
         torch.cuda.synchronize()
         runs[chunk] = {k: o[k] for k in ("idx", "out", "lse")}
-    for chunk in (8192, 2048):
+    # 2k chunks again with steps 1-2 fused (no score matrix)
+    say("prefill 17k: chunk 2048, indexer + select fused")
+    o = prefill.alloc_prompt_outputs(cfg)
+    prefill.run_prefill(cfg, dev, 2048, o, fused=True)
+    torch.cuda.synchronize()
+    runs["2048-fused"] = {k: o[k] for k in ("idx", "out", "lse")}
+    for chunk in (8192, 2048, "2048-fused"):
         for key in ("idx", "out", "lse"):
             assert torch.equal(runs[chunk][key], runs[T][key]), (chunk, key)
     edges = sorted({r for c in range(0, T, 2048) for r in (c - 1, c, c + 1) if 0 <= r < T} | {T - 1})
