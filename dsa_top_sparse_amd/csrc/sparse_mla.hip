@@ -17,7 +17,8 @@
 // form the M = 64 side of both products and no MFMA lane is wasted on
 // masking. Per tile of 32 selected slots:
 //   gather  : all waves issue direct-to-LDS 16-byte loads of the selected
-//             rows, two tiles ahead, into one of 4 LDS stages;
+//             rows, two tiles ahead, into one of 4 LDS stages (latent parts
+//             in four 8 KB groups of 128 dims, then the rope parts);
 //   Q K^T   : score waves 0-3 each own 32 heads x 16 slots; S^T = K Q^T on
 //             16x16x32 bf16 MFMAs with the query's Q fragments in registers;
 //   softmax : fp32, exp2 with log2(e) folded into the scale, against a fixed
@@ -25,7 +26,7 @@
 //             (split into hi + lo bf16 parts when the query has few valid
 //             keys, where single bf16 rounding of a large weight would show);
 //   P V     : P V waves 4-7 each own output dims 128v..128v+127 of all 64
-//             heads, reading V transposed out of the key-major stage.
+//             heads, reading V transposed out of the stage.
 // The two roles run side by side on every SIMD, one tile apart, and meet at
 // one barrier per tile (details at the kernel).
 #include <mutex>
