@@ -107,3 +107,44 @@ def test_fused_outside_the_fused_kernels(torch_cuda, shape):
     off = shape[3] if len(shape) > 3 else 3000
     cfg = _cfg(n_q=8 if off > 60000 else 50, offset=off, n_idx_heads=h, d_idx=d, idx_dtype=dt, seed=76 + h)
     _check(torch_cuda, cfg, synth.generate(cfg), f"outside {shape}", with_oracle=off < 60000)
+
+
+def test_prefill_chunk_fused_at_long_context(torch_cuda):
+    # One chunk of 512 queries at a 34k-key context (where the prefill driver
+    # runs steps 1-2 fused) through dsa_prefill_chunk, once with a score
+    # matrix and once with NULL scores: caches, indices, outputs and lse
+    # bit-identical; a few rows' indices against the oracle.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C3"].replace(name="fused_prefill", n_q=512, offset=33800, seed=11)
+    say(f"fused prefill: generate {cfg}")
+    inputs = synth.generate(cfg)
+    dev = binding.to_device(inputs)
+    dims = binding.make_dims(cfg)
+    T = cfg.offset + cfg.n_q
+    r = slice(cfg.offset, T)
+    runs = {}
+    for mode in ("scores", "fused"):
+        kv = dev["kv"].clone()
+        kx = dev["kidx"].clone()
+        kv_chunk = dev["kv"][r].clone()
+        kx_chunk = dev["kidx"][r].clone()
+        kv[r] = 0  # the call appends the chunk's rows
+        kx[r] = 0
+        idx = torch.full((cfg.n_q, cfg.top_k), 12345, dtype=torch.int32, device="cuda")
+        out = torch.empty((cfg.n_q, cfg.n_heads, cfg.d_latent), dtype=torch.float32, device="cuda")
+        lse = torch.empty((cfg.n_q, cfg.n_heads), dtype=torch.float32, device="cuda")
+        if mode == "scores":
+            scores = torch.empty((cfg.n_q, T), dtype=torch.float32, device="cuda")
+            binding.prefill_chunk(dims, dev["q"], kv_chunk, dev["qidx"], dev["w"], kx_chunk, kv, kx, scores, T,
+                                  idx, out, lse)
+        else:
+            ws = torch.empty(binding.indexer_topk_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+            binding.prefill_chunk(dims, dev["q"], kv_chunk, dev["qidx"], dev["w"], kx_chunk, kv, kx, None, 0,
+                                  idx, out, lse, ws)
+        torch.cuda.synchronize()
+        runs[mode] = (kv, kx, idx, out, lse)
+    for a, b, what in zip(runs["scores"], runs["fused"], ("kv cache", "k_idx cache", "idx", "out", "lse")):
+        assert torch.equal(a, b), what
+    rows = [0, 255, 511]
+    ref = oracle.full_path(cfg, inputs, rows=rows)
+    assert np.array_equal(runs["fused"][2][rows].cpu().numpy(), ref["idx"])
