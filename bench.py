@@ -83,10 +83,10 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, inputs, target_s: float):
+def cpu_baseline(cfg, inputs, target_s: float, tiny: bool = True):
     """The oracle (untuned) on the host cores, on a bounded sample of the same
-    chunk's query rows: all three steps timed one after the other; plus the
-    tiny workload on one core."""
+    chunk's query rows: all three steps timed one after the other; plus
+    (tiny) the tiny workload on one core."""
     import numpy as np
     import oracle
     from dsa_top_sparse_amd import synth
@@ -110,6 +110,12 @@ def cpu_baseline(cfg, inputs, target_s: float):
     st = staged(cfg, inputs, rows)
     t = sum(st)
     cores = oracle.num_threads()
+    res = {"value": round(len(rows) / t, 2), "unit": UNIT, "cores": cores, "kind": "oracle",
+           "sample": f"{len(rows)} evenly spaced query rows of the same chunk, all three steps, {t:.1f} s",
+           "cpu_model": cpu_model(),
+           "stage_s": {"indexer": round(st[0], 3), "select": round(st[1], 3), "attention": round(st[2], 3)}}
+    if not tiny:
+        return res
     # the tiny fp32 workload, every row, on one core
     c0 = synth.CONFIGS["C0"]
     c0_in = synth.generate(c0)
@@ -118,12 +124,71 @@ def cpu_baseline(cfg, inputs, target_s: float):
         t0 = sum(staged(c0, c0_in, None))
     finally:
         oracle.set_threads(cores)
-    return {"value": round(len(rows) / t, 2), "unit": UNIT, "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} evenly spaced query rows of the same chunk, all three steps, {t:.1f} s",
-            "cpu_model": cpu_model(),
-            "stage_s": {"indexer": round(st[0], 3), "select": round(st[1], 3), "attention": round(st[2], 3)},
-            "one_core_tiny": {"workload": c0.name, "rows": c0.n_q, "s": round(t0, 4),
-                              "value": round(c0.n_q / t0, 1), "unit": UNIT}}
+    res["one_core_tiny"] = {"workload": c0.name, "rows": c0.n_q, "s": round(t0, 4),
+                            "value": round(c0.n_q / t0, 1), "unit": UNIT}
+    return res
+
+
+def measure_peaks(torch, stream):
+    """This device's achievable dense bf16 matrix-core rate and HBM copy rate,
+    from the hand-written micro-kernels of libdsa_peaks.so (best of 3 runs
+    each, HIP events on the launch stream)."""
+    import ctypes
+    from dsa_top_sparse_amd import build as hip_build
+    try:
+        L = ctypes.CDLL(hip_build.PEAKS_LIB)
+    except OSError as e:
+        return {"error": f"measurement library not built: {e}"}
+    L.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    blocks, iters = 512, 16
+    sink = torch.empty(blocks * 1024, dtype=torch.float32, device="cuda")
+    flops = blocks * 16 * iters * 16 * 8 * 16384.0
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        fn()
+        times = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        return min(times)
+
+    def mfma():
+        assert L.dsa_peak_mfma(blocks, iters, sink.data_ptr(), stream.cuda_stream) == 0
+
+    def copy():
+        assert L.dsa_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream.cuda_stream) == 0
+    t_mfma = best(mfma)
+    t_copy = best(copy)
+    assert torch.equal(dst[:1024], src[:1024])
+    del sink, src, dst
+    return {"mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1), "copy_GBs": round(2 * nbytes / t_copy / 1e9, 1),
+            "method": "16x16x32 bf16 MFMA loop (16 waves x 8 chains per CU) and a 1 GiB 16-byte-per-lane copy "
+                      "(bytes read + written), best of 3"}
+
+
+def block_unions(torch, idx, k, blocks=(2, 4, 8, 16, 64)):
+    """Distinct selected keys per query if blocks of B consecutive queries
+    shared their gathered rows (the pages' block-sparse proposal): the mean
+    union size per query, and its ratio to k."""
+    out = {}
+    n = idx.shape[0]
+    for B in blocks:
+        m = (n // B) * B
+        v = idx[:m].reshape(m // B, B * idx.shape[1]).sort(dim=1).values
+        valid = v >= 0
+        distinct = ((v[:, 1:] != v[:, :-1]) & valid[:, 1:]).sum(dim=1) + valid[:, 0].to(torch.int64)
+        per_q = distinct.double().mean().item() / B
+        out[str(B)] = {"keys_per_query": round(per_q, 1), "over_k": round(per_q / k, 3)}
+    return out
 
 
 # The pages' per-layer rate for the same replay (8,192 tokens in 2,048-token
@@ -367,6 +432,10 @@ def main():
     if args.path == "fused":
         fused_ws = torch.empty(binding.indexer_topk_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
     timing = time_workload(torch, binding, cfg, dev, outs, stream, args.steps, args.warmup, flush, fused_ws=fused_ws)
+    # best of 3 shorter batches beside the contract's one bracket
+    nb = max(5, args.steps // 2)
+    best_batch = min(time_workload(torch, binding, cfg, dev, outs, stream, nb, 0, flush, fused_ws=fused_ws)["wall"] / nb
+                     for _ in range(3))
     wall = timing["wall"]
     avg, med, mn = timing["avg"], timing["med"], timing["min"]
     ms_per_step = 1e3 * wall / args.steps
@@ -400,13 +469,17 @@ def main():
         kernels["attention"]["cold_ms"] = cold_k["attention"]["ms"]
         kernels["attention"]["cold_mfma_frac"] = cold_k["attention"]["mfma_frac"]
     workloads = None
+    workloads_cpu = {}
     if args.replay:
         workloads = {}
         for other in ("C2", "C4"):
             ocfg = synth.CONFIGS[other]
-            odev = binding.to_device(synth.generate(ocfg))
+            oinputs = synth.generate(ocfg)
+            odev = binding.to_device(oinputs)
             oouts = binding.alloc_outputs(ocfg)
             t = time_workload(torch, binding, ocfg, odev, oouts, stream, 10, 3, None)
+            if args.cpu_baseline_s > 0:
+                workloads_cpu[ocfg.name] = (ocfg, oinputs)
             workloads[ocfg.name] = {"ms_per_step": round(1e3 * t["wall"] / 10, 4),
                                     "query_tokens_per_s": round(ocfg.n_q * 10 / t["wall"], 1),
                                     "kernels": kernel_summary(ocfg, t["avg"]),
@@ -419,6 +492,12 @@ def main():
     cpu = None
     if args.cpu_baseline_s > 0:
         cpu = cpu_baseline(cfg, inputs, args.cpu_baseline_s)
+        for name, (ocfg, oinputs) in workloads_cpu.items():  # shorter samples of the other workloads
+            workloads[name]["cpu_baseline"] = cpu_baseline(ocfg, oinputs, args.cpu_baseline_s / 4, tiny=False)
+    peaks = measure_peaks(torch, stream) if args.replay else None
+    unions = block_unions(torch, outs["idx"], cfg.top_k) if args.replay else None
+    if peaks and "mfma_bf16_tflops" in peaks:
+        roofline["frac_of_measured_peak"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
     line = {
         "metric": METRIC, "value": round(cfg.n_q * args.steps / wall, 1), "unit": UNIT, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -429,7 +508,12 @@ def main():
                    "indexer": f"{cfg.n_idx_heads}x{cfg.d_idx}", "mode": "cold" if args.cold else "warm",
                    "path": args.path},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "best_batch_ms_per_step": round(1e3 * best_batch, 4),
     }
+    if peaks is not None:
+        line["measured_peaks"] = peaks
+    if unions is not None:
+        line["block_union"] = unions
     if paths is not None:
         line["paths"] = paths
     if workloads is not None:

@@ -10,6 +10,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa_amd.so")
+# measurement micro-kernels (the benchmark's achievable-peak figures), a library of their own
+PEAKS_LIB = os.path.join(PKG, "libdsa_peaks.so")
+PEAKS_SOURCE = "peaks.hip"
 SOURCES = ["dsa_api.cpp", "validate.cpp", "selftest.hip", "indexer.hip", "topk.hip", "fused.hip", "sparse_mla.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -52,6 +55,23 @@ def build(extra_flags=None, out: str = LIB) -> str:
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+    if out == LIB:
+        build_peaks()
+    return out
+
+
+def build_peaks(out: str = PEAKS_LIB) -> str:
+    """Compile the measurement micro-kernels into their own shared library."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    obj = os.path.join(objdir, "peaks.o")
+    _compile(PEAKS_SOURCE, obj, [])
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp], capture_output=True,
+                       text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)

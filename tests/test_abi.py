@@ -179,3 +179,19 @@ def test_decode_noalloc_rejects_before_the_device(L):
     assert call(dims(n_q=4), lse=FAKE + 4) == ALIGN
     assert call(dims(n_q=4, top_k=0)) == SHAPE
     assert call(dims(n_q=0), q=None, kv=None, idx=None, out=None) == OK
+
+
+def test_measurement_library_exports():
+    # the benchmark's micro-kernel library (achievable MFMA and copy rates):
+    # built beside the product library, its two entry points exported, and its
+    # argument checks answer before any launch
+    from dsa_top_sparse_amd import build as hip_build
+    if not os.path.exists(hip_build.PEAKS_LIB):
+        pytest.skip("measurement library not built")
+    P = ctypes.CDLL(hip_build.PEAKS_LIB)
+    P.dsa_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert P.dsa_peak_mfma(0, 1, FAKE, None) != 0
+    assert P.dsa_peak_mfma(1, 1, None, None) != 0
+    assert P.dsa_peak_copy(FAKE, FAKE, 17, None) != 0
+    assert P.dsa_peak_copy(None, FAKE, 16, None) != 0
