@@ -67,22 +67,44 @@ __device__ __forceinline__ void fill_neg_inf(float* __restrict__ scores, int64_t
   }
 }
 
+// Work unit of workgroup bid: (key range kr of keys_per_unit keys, 64-query
+// block qb); false if the workgroup has none. Workgroups reach the 8 XCDs in
+// turn (XCD = bid % 8). With a multiple of 8 query blocks, XCD x takes the
+// query blocks qb = x (mod 8) of every key range, latest (most causal keys)
+// first, and visits the key ranges from x * n_kr / 8 on. Every XCD then gets
+// the same share of the causal work (a contiguous run of units per XCD left
+// the XCDs holding the early key ranges with a third more work than the mean
+// on an 8k chunk at an 8k offset), each XCD holds only a few key ranges in
+// its L2 at a time, and the workgroups resident on the chip write into all key
+// ranges of their score rows at once instead of a narrow band of columns.
+// Otherwise XCD x takes a contiguous run of units.
+__device__ __forceinline__ bool unit_of(int bid, int n_qb, int n_units, int units_per_xcd, int& kr, int& qb) {
+  if ((n_qb & 7) == 0) {
+    const int x = bid & 7, k = bid >> 3, per = n_qb >> 3;
+    const int n_kr = n_units / n_qb;
+    const int jr = k / per, i = k - jr * per;
+    if (jr >= n_kr) return false;
+    kr = (jr + x * (n_kr >> 3)) % n_kr;
+    qb = 8 * (per - 1 - i) + x;
+    return true;
+  }
+  const int u = (bid & 7) * units_per_xcd + (bid >> 3);
+  if (u >= n_units) return false;
+  kr = u / n_qb;
+  qb = u - kr * n_qb;
+  return true;
+}
+
 // bf16, 4 indexer heads, d_idx = D (multiple of 16).
-// Work unit = (64-query block, range of `keys_per_unit` keys). Units are laid
-// out so that the units one XCD runs share a key range: workgroups are handed
-// to the 8 XCDs round-robin, so unit u = xcd * units_per_xcd + slot keeps the
-// indexer keys of one range hot in that XCD's L2 while the queries stream.
+// Work unit = (64-query block, range of `keys_per_unit` keys), see unit_of.
 template <int D>
 __global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
     int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
     int n_units, int units_per_xcd, int keys_per_unit) {
   constexpr int KS = D / 16;  // k-steps of the 32x32x16 MFMA
-  const int bid = blockIdx.x;
-  const int u = (bid & 7) * units_per_xcd + (bid >> 3);
-  if (u >= n_units) return;
-  const int kr = u / n_qb;
-  const int qb = u - kr * n_qb;
+  int kr, qb;
+  if (!unit_of((int)blockIdx.x, n_qb, n_units, units_per_xcd, kr, qb)) return;
   const int q0 = qb * kIdxQueries;
   const int nrows = min(kIdxQueries, n_q - q0);
   const int64_t k_begin = (int64_t)kr * keys_per_unit;
@@ -190,11 +212,8 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
     int n_units, int units_per_xcd, int keys_per_unit, IndexerCandidates fo) {
   constexpr int D = 128, KS = D / 16;
-  const int bid = blockIdx.x;
-  const int u = (bid & 7) * units_per_xcd + (bid >> 3);
-  if (u >= n_units) return;
-  const int kr = u / n_qb;
-  const int qb = u - kr * n_qb;
+  int kr, qb;
+  if (!unit_of((int)blockIdx.x, n_qb, n_units, units_per_xcd, kr, qb)) return;
   const int q0 = qb * kIdxQueries;
   const int nrows = min(kIdxQueries, n_q - q0);
   const int64_t k_begin = (int64_t)kr * keys_per_unit;
