@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets wave-level tests branch on scalars
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -317,9 +317,11 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
       }
       // register r of lane (l32, hi): query 2 (r / 4) + hi of the 8-query group, head r % 4, key l32.
       // ReLU as an integer max on the bits (one instruction: a negative float is a
-      // negative int32); adding +0 turns a -0 sum into +0;
-      // the causal mask is needed only where the block reaches the wave's
-      // first query (block-uniform test).
+      // negative int32). No score comes out as -0: the head sum starts as
+      // fma(w, x, +0), and under round-to-nearest an exactly zero sum of
+      // nonzero terms, or of zeros of both signs, is +0. The causal mask is
+      // needed only where the block reaches the wave's first query
+      // (wave-uniform test).
       if (FILTER) {
         // the lane's causal scores >= its query's threshold, in key order,
         // to that query's segment of this key range
@@ -330,7 +332,6 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
           for (int h = 0; h < 4; ++h)
             sc = fmaf(sw[qrow][h], __int_as_float(max(__float_as_int(acc[0][4 * g + h]), 0)), sc);
-          sc = sc + 0.0f;
           const bool keep = key <= (int64_t)offset + q0 + qrow && sc >= (hi ? tf_hi[g] : tf_lo[g]);
           const uint64_t m = __ballot(keep);
           const uint32_t m_lo = static_cast<uint32_t>(m), m_hi = static_cast<uint32_t>(m >> 32);
@@ -350,22 +351,30 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
         // Through this wave's LDS tile, so that the stores are 16-byte vectors
         // (4 keys of one query per lane) instead of one score per lane.
         float* tb = tbuf[wave];
+        // Score of row qr (of the wave's 8 queries) for the lane's key.
+        auto head_sum = [&](int g, int qr) {
+          float sc = 0.0f;
 #pragma unroll
-        for (int mb = 0; mb < 1; ++mb)
+          for (int h = 0; h < 4; ++h)
+            sc = fmaf(sw[wave * 8 + qr][h], __int_as_float(max(__float_as_int(acc[0][4 * g + h]), 0)), sc);
+          return sc;
+        };
+        if (all_causal) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) tb[(2 * g + hi) * kTbRow + l32] = head_sum(g, 2 * g + hi);
+        } else {
+          // key nb + l32 is causal for row qr iff l32 + rel <= qr; here
+          // -32 < rel < 64 (the sub-block reaches the wave's first query and
+          // starts at or before the block's last one)
+          const int rel = (int)(nb - ((int64_t)offset + q0 + wave * 8));
+          const int lk = l32 + rel;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int qr = 2 * g + hi;  // row inside the wave's 8 queries
-            float sc = 0.0f;
-#pragma unroll
-            for (int h = 0; h < 4; ++h)
-              sc = fmaf(sw[wave * 8 + qr][h], __int_as_float(max(__float_as_int(acc[mb][4 * g + h]), 0)), sc);
-            sc = sc + 0.0f;
-            if (!all_causal) {
-              const int64_t p = (int64_t)offset + q0 + wave * 8 + qr;
-              sc = key <= p ? sc : -INFINITY;
-            }
-            tb[qr * kTbRow + l32] = sc;
+            const int qr = 2 * g + hi;
+            const float sc = head_sum(g, qr);
+            tb[qr * kTbRow + l32] = lk <= qr ? sc : -INFINITY;
           }
+        }
 #pragma unroll
         for (int x = 0; x < 1; ++x) {
           const int piece = 64 * x + lane, r = piece >> 3, c = piece & 7;
@@ -384,7 +393,6 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
             for (int h = 0; h < 4; ++h)
               sc = fmaf(sw[qrow][h], __int_as_float(max(__float_as_int(acc[mb][4 * g + h]), 0)), sc);
-            sc = sc + 0.0f;
             if (!all_causal) {
               const int64_t p = (int64_t)offset + q0 + qrow;
               sc = key <= p ? sc : -INFINITY;
