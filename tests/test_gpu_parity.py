@@ -128,6 +128,31 @@ def test_ragged_fast_path_all_rows(torch_cuda, ld_pad):
     check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], "ragged")
 
 
+@pytest.mark.parametrize("n_q,offset,d_idx", [
+    (512, 0, 128),     # 8 query blocks, 4 key ranges: every XCD's walk starts at the first range
+    (1024, 3000, 128),  # 16 query blocks, 32 key ranges: staggered walks, 2 blocks per XCD and range
+    (576, 700, 128),    # 9 query blocks: contiguous runs of units per XCD
+    (512, 2000, 64),    # the per-wave indexer (d_idx 64) on the staggered walk
+])
+def test_indexer_unit_walks(torch_cuda, n_q, offset, d_idx):
+    # The indexer maps workgroups to (key range, query block) units by a
+    # staggered walk per XCD when the query blocks are a multiple of 8 and by
+    # contiguous runs otherwise. Every score of every row, bit-exact, on a
+    # buffer filled with NaN first, so that a unit left out shows.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C2"].replace(name=f"units_{n_q}_{offset}_{d_idx}", n_q=n_q, offset=offset, d_idx=d_idx,
+                                      seed=n_q + offset + d_idx)
+    _say(f"indexer unit walk: {cfg}")
+    inputs = synth.generate(cfg)
+    dev = binding.to_device(inputs)
+    ld = cfg.t_ctx
+    scores = torch.full((cfg.n_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+    binding.indexer_scores(binding.make_dims(cfg), dev["qidx"], dev["w"], dev["kidx"], scores, ld)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_scores(cfg.n_q, cfg.offset, inputs["qidx"], inputs["w"], inputs["kidx"], ld=ld)
+    assert np.array_equal(scores.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 def test_small_contexts_dense_and_hilo(torch_cuda):
     # offset 0, 100 queries, k = 2048: every row is dense causal with 1..100
     # keys, the few-key regime where P is split into hi + lo bf16 parts.
