@@ -143,6 +143,8 @@ constexpr int kThreads = 512;       // 8 waves: 4 score waves + 4 P V waves
 constexpr int kStages = 4;          // LDS tile stages (hi/lo queries use 3; P's lo part takes the 4th)
 constexpr int kRowBytes = kDQK * 2;              // 1152 = 72 pieces of 16 bytes
 constexpr int kStageBytes = kTile * kRowBytes;   // 36 KB
+constexpr int kOPad = 132;  // floats per head row of a P V wave's staged O (128 dims + 4: conflict-free writes)
+static_assert(4 * kH * kOPad * 4 <= kStages * kStageBytes, "staged O of the 4 P V waves fits in the stages");
 static_assert(kStageBytes % 256 == 0, "stage bases leave the low 8 address bits alone");
 constexpr int kRingTiles = 32;      // index ring: 4 parts of 8 tiles (1 KB each)
 constexpr int kHiloMaxValid = 512;  // queries with at most this many valid keys use hi/lo P
@@ -654,6 +656,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
       const float lh = sum_over_q4(l_part[hb]);
       if (q4 == 0) sm.lsum[s][head[hb]] = lh;
     }
+    wait_vmcnt<0>();  // no tile load in flight: the P V waves reuse the stages for O
     __syncthreads();  // E1
     if (lse && s == 0 && q4 == 0) {
 #pragma unroll
@@ -766,9 +769,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
       lds_barrier();  // Z2
       pass(false);
     }
-    // ---- epilogue: O / l.
-    __syncthreads();  // E1: denominators published
-    float* __restrict__ orow = out + out_row * kH * kDL + 128 * v + l16;
+    // ---- epilogue: O / l, staged through LDS so that every store writes
+    // whole 128-byte lines. A lane holds one dim of four heads (16 lanes: 64
+    // contiguous bytes of a head row); through the stages, which no wave reads
+    // or loads after E1, each lane stores 4 consecutive dims of one head, and
+    // one store instruction two 512-byte pieces of head rows.
+    wait_vmcnt<0>();
+    __syncthreads();  // E1: denominators published, stages free
+    float* ob = reinterpret_cast<float*>(&sm.stage[0][0]) + v * (kH * kOPad);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       float f[4];
@@ -781,8 +789,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          __builtin_nontemporal_store(o[mb][nb][r] * f[r], orow + (int64_t)(16 * mb + 4 * q4 + r) * kDL + 16 * nb);
+        for (int r = 0; r < 4; ++r) ob[(16 * mb + 4 * q4 + r) * kOPad + 16 * nb + l16] = o[mb][nb][r] * f[r];
+    }
+    float* __restrict__ orow = out + out_row * kH * kDL + 128 * v + 4 * (lane & 31);
+#pragma unroll
+    for (int j = 0; j < kH / 2; ++j) {
+      const int hh = 2 * j + (lane >> 5);
+      const f32x4 val = *reinterpret_cast<const f32x4*>(&ob[hh * kOPad + 4 * (lane & 31)]);
+      __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(orow + (int64_t)hh * kDL));
     }
   };
 
