@@ -153,6 +153,36 @@ def test_indexer_unit_walks(torch_cuda, n_q, offset, d_idx):
     assert np.array_equal(scores.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("d_idx", [128, 64])
+def test_indexer_negative_weights_and_zero_sums(torch_cuda, d_idx):
+    # Weights in {-2, -1, 1, 2}: the small-integer indexer products stay exact,
+    # so scores are still bit-exact; head sums cancel to exactly zero and
+    # negative weights meet ReLU zeros, and every zero must come out as +0.
+    # d_idx 128 runs the LDS-staged indexer, 64 the per-wave one.
+    torch = torch_cuda
+    cfg = synth.CONFIGS["C2"].replace(name=f"negw_{d_idx}", n_q=200, offset=900, d_idx=d_idx, top_k=256,
+                                      seed=77 + d_idx)
+    _say(f"negative weights: {cfg}")
+    inputs = synth.generate(cfg)
+    rng = np.random.default_rng(cfg.seed)
+    inputs["w"] = rng.choice(np.array([-2.0, -1.0, 1.0, 2.0], dtype=np.float32), size=inputs["w"].shape)
+    dev, outs = run_gpu(torch, cfg, inputs)
+    dims = binding.make_dims(cfg)
+    ws = torch.empty(max(1, binding.indexer_topk_workspace_bytes(dims)), dtype=torch.uint8, device="cuda")
+    fidx = torch.full_like(outs["idx"], 12345)
+    binding.indexer_topk(dims, dev["qidx"], dev["w"], dev["kidx"], fidx, ws)
+    torch.cuda.synchronize()
+    ref = oracle.full_path(cfg, inputs)
+    s = outs["scores"].cpu().numpy()
+    assert np.array_equal(s.view(np.uint32), ref["scores"].view(np.uint32))
+    zeros = s == 0.0
+    assert zeros.sum() > 1000 and not np.signbit(s[zeros]).any()
+    assert (s < 0).any()  # negative scores occur and are kept as they are
+    assert np.array_equal(outs["idx"].cpu().numpy(), ref["idx"])
+    assert np.array_equal(fidx.cpu().numpy(), ref["idx"])
+    check_attention(outs["out"].cpu().numpy(), outs["lse"].cpu().numpy(), ref["out"], ref["lse"], cfg.name)
+
+
 def test_small_contexts_dense_and_hilo(torch_cuda):
     # offset 0, 100 queries, k = 2048: every row is dense causal with 1..100
     # keys, the few-key regime where P is split into hi + lo bf16 parts.
