@@ -319,7 +319,8 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
       // ReLU as an integer max on the bits (one instruction: a negative float is a
       // negative int32). No score comes out as -0: the head sum starts as
       // fma(w, x, +0), and under round-to-nearest an exactly zero sum of
-      // nonzero terms, or of zeros of both signs, is +0. The causal mask is
+      // nonzero terms, or of zeros of both signs, is +0 (fp32 denormals are
+      // kept, so no tiny result flushes to -0). The causal mask is
       // needed only where the block reaches the wave's first query
       // (wave-uniform test).
       if (FILTER) {
