@@ -6,6 +6,7 @@ raises if the library has not been built -- there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Dict, Optional
@@ -65,39 +66,57 @@ class DsaError(RuntimeError):
 _lib = None
 
 
+def _load(path: str) -> ctypes.CDLL:
+    """Loads one build of the HIP library and declares its entry points."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() "
+                           "(or python -m dsa_top_sparse_amd.build) first")
+    L = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    dp = ctypes.POINTER(Dims)
+    L.dsa_indexer_scores.argtypes = [dp, vp, vp, vp, vp, i64, vp]
+    L.dsa_topk_workspace_bytes.argtypes = [dp]
+    L.dsa_topk_workspace_bytes.restype = sz
+    L.dsa_topk_select.argtypes = [dp, vp, i64, vp, vp, sz, vp]
+    L.dsa_sparse_mla_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    L.dsa_indexer_topk_workspace_bytes.argtypes = [dp]
+    L.dsa_indexer_topk_workspace_bytes.restype = sz
+    L.dsa_indexer_topk.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_decode_workspace_bytes.argtypes = [dp]
+    L.dsa_sparse_mla_decode_workspace_bytes.restype = sz
+    L.dsa_sparse_mla_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_indexer_topk, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk,
+              L.dsa_sparse_mla_decode, L.dsa_sparse_mla_decode_noalloc):
+        f.restype = ctypes.c_int
+    L.dsa_self_test.argtypes = []
+    L.dsa_self_test.restype = ctypes.c_int
+    L.dsa_status_string.argtypes = [ctypes.c_int]
+    L.dsa_status_string.restype = ctypes.c_char_p
+    L.dsa_version.restype = ctypes.c_int32
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Loads the HIP library (raises if it is missing: build it first)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() "
-                               "(or python -m dsa_top_sparse_amd.build) first")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
-        dp = ctypes.POINTER(Dims)
-        L.dsa_indexer_scores.argtypes = [dp, vp, vp, vp, vp, i64, vp]
-        L.dsa_topk_workspace_bytes.argtypes = [dp]
-        L.dsa_topk_workspace_bytes.restype = sz
-        L.dsa_topk_select.argtypes = [dp, vp, i64, vp, vp, sz, vp]
-        L.dsa_sparse_mla_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp]
-        L.dsa_indexer_topk_workspace_bytes.argtypes = [dp]
-        L.dsa_indexer_topk_workspace_bytes.restype = sz
-        L.dsa_indexer_topk.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
-        L.dsa_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
-        L.dsa_sparse_mla_decode_workspace_bytes.argtypes = [dp]
-        L.dsa_sparse_mla_decode_workspace_bytes.restype = sz
-        L.dsa_sparse_mla_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.dsa_sparse_mla_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp]
-        for f in (L.dsa_indexer_scores, L.dsa_topk_select, L.dsa_indexer_topk, L.dsa_sparse_mla_fwd, L.dsa_prefill_chunk,
-                  L.dsa_sparse_mla_decode, L.dsa_sparse_mla_decode_noalloc):
-            f.restype = ctypes.c_int
-        L.dsa_self_test.argtypes = []
-        L.dsa_self_test.restype = ctypes.c_int
-        L.dsa_status_string.argtypes = [ctypes.c_int]
-        L.dsa_status_string.restype = ctypes.c_char_p
-        L.dsa_version.restype = ctypes.c_int32
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Inside the block, every call of this module goes to another build of
+    the library at `path` (the tests use the LDS-poisoned debug build)."""
+    global _lib
+    saved = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def status_string(status: int) -> str:

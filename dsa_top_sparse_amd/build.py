@@ -12,6 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa_amd.so")
 # measurement micro-kernels (the benchmark's achievable-peak figures), a library of their own
 PEAKS_LIB = os.path.join(PKG, "libdsa_peaks.so")
+# debug build of the same sources whose kernels fill their LDS with NaN first (tests only)
+LDS_POISON_LIB = os.path.join(PKG, "libdsa_amd_lds_poison.so")
 PEAKS_SOURCE = "peaks.hip"
 SOURCES = ["dsa_api.cpp", "validate.cpp", "selftest.hip", "indexer.hip", "topk.hip", "fused.hip", "sparse_mla.hip"]
 ARCH = "gfx950"
@@ -47,7 +49,7 @@ def _compile(src: str, obj: str, extra) -> None:
 def build(extra_flags=None, out: str = LIB) -> str:
     """Compile every source and link the shared library. Returns its path."""
     extra = list(extra_flags or [])
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(PKG, "_build", os.path.splitext(os.path.basename(out))[0])
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -60,6 +62,7 @@ def build(extra_flags=None, out: str = LIB) -> str:
     os.replace(tmp, out)
     if out == LIB:
         build_peaks()
+        build(["-DDSA_LDS_POISON"], LDS_POISON_LIB)
     return out
 
 

@@ -55,4 +55,21 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
+// Debug builds (-DDSA_LDS_POISON) fill the workgroup's LDS -- the static part
+// and `dyn_bytes` of dynamic LDS after it -- with a NaN pattern before the
+// kernel body runs, so that a read of LDS the kernel never wrote shows in its
+// results. Every kernel calls it first, before any early return (it ends in a
+// barrier); the product build compiles it to nothing.
+__device__ __forceinline__ void lds_poison(uint32_t dyn_bytes = 0) {
+#ifdef DSA_LDS_POISON
+  const uint32_t words = (__builtin_amdgcn_groupstaticsize() + dyn_bytes) / 4u;
+  for (uint32_t w = threadIdx.x; w < words; w += blockDim.x)
+    asm volatile("ds_write_b32 %0, %1" ::"v"(4u * w), "v"(0x7FC00001u) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+#else
+  (void)dyn_bytes;
+#endif
+}
+
 }  // namespace dsa

@@ -37,6 +37,7 @@ static_assert(kFusedMaxRow / 128 <= kMaxUnits, "a query's key ranges fit the off
 // its first min(n, 2048) keys (sample row i, 2048 floats a row).
 __global__ __launch_bounds__(kFsThreads) void tau_kernel(int offset, int k, const float* __restrict__ sample,
                                                          uint32_t* __restrict__ tau_out, float* __restrict__ tf_out) {
+  lds_poison();
   __shared__ FsSmem sm;
   int buf = 0;
   const int i = blockIdx.x;
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(kFsThreads) void cand_select_kernel(int offset, int
                                                                  const float* __restrict__ w,
                                                                  const uint16_t* __restrict__ k_idx,
                                                                  int32_t* __restrict__ idx) {
+  lds_poison();
   __shared__ FsSmem sm;
   __shared__ uint32_t uoff[kMaxUnits + 1];
   int buf = 0;

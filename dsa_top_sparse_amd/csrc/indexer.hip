@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void indexer_plain_kernel(int n_q, int offset,
                                                             const float* __restrict__ w,
                                                             const T* __restrict__ k_idx,
                                                             float* __restrict__ scores, int64_t ld) {
+  lds_poison(4u * (uint32_t)(n_heads * d_idx));  // sq[]
   extern __shared__ float sq[];  // [n_heads][d_idx] of this query
   const int i = blockIdx.y;
   const int hd = n_heads * d_idx;
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_mfma_kernel(
     int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
     int n_units, int units_per_xcd, int keys_per_unit) {
+  lds_poison();
   constexpr int KS = D / 16;  // k-steps of the 32x32x16 MFMA
   int kr, qb;
   if (!unit_of((int)blockIdx.x, n_qb, n_units, units_per_xcd, kr, qb)) return;
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(kIdx8Threads) __attribute__((amdgpu_waves_per_eu(4)
     int n_q, int offset, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, float* __restrict__ scores, int64_t ld, int n_qb,
     int n_units, int units_per_xcd, int keys_per_unit, IndexerCandidates fo) {
+  lds_poison();
   constexpr int D = 128, KS = D / 16;
   int kr, qb;
   if (!unit_of((int)blockIdx.x, n_qb, n_units, units_per_xcd, kr, qb)) return;

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kPlainThreads) void mla_plain_kernel(int offset, in
                                                                   const int32_t* __restrict__ idx,
                                                                   float* __restrict__ out,
                                                                   float* __restrict__ lse) {
+  lds_poison(4u * (uint32_t)(d_qk + 2 * top_k));  // smem[]
   extern __shared__ float smem[];
   float* sq = smem;                                            // [d_qk]
   float* sw = sq + d_qk;                                       // [top_k] logits, then weights
@@ -366,6 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_mfma_kernel(int n_q, int offs
                                                                const uint16_t* __restrict__ kv,
                                                                const int32_t* __restrict__ idx,
                                                                float* __restrict__ out, float* __restrict__ lse) {
+  lds_poison();
   __shared__ __attribute__((aligned(1024))) MlaSmem sm;
   const int i = n_q - 1 - (int)blockIdx.x;  // latest queries (most keys) first
   const int split = blockIdx.y;
@@ -843,6 +845,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(int n_q, i
                                                                       const float* __restrict__ part_out,
                                                                       const float* __restrict__ part_lse,
                                                                       float* __restrict__ out, float* __restrict__ lse) {
+  lds_poison();
   const int i = blockIdx.x, h = blockIdx.y;
   float m = -INFINITY;
   for (int s = 0; s < splits; ++s) m = fmaxf(m, part_lse[((int64_t)s * n_q + i) * kH + h]);

@@ -285,6 +285,7 @@ __device__ __forceinline__ void select_tail(TopkSmem& sm, int& buf, const float*
 template <bool ALIGNED>
 __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, const float* __restrict__ scores,
                                                           int64_t ld, int32_t* __restrict__ idx) {
+  lds_poison();
   __shared__ TopkSmem sm;
   int buf = 0;
   const int i = blockIdx.x;
@@ -445,6 +446,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(int offset, int k, con
 // candidates; a row the sample misleads is selected again without it.
 __global__ __launch_bounds__(kFsThreads) void topk_filter_kernel(int offset, int k, const float* __restrict__ scores,
                                                                  int64_t ld, int32_t* __restrict__ idx) {
+  lds_poison();
   __shared__ FsSmem sm;
   int buf = 0;
   const int i = blockIdx.x;

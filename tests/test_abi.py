@@ -195,3 +195,21 @@ def test_measurement_library_exports():
     assert P.dsa_peak_mfma(1, 1, None, None) != 0
     assert P.dsa_peak_copy(FAKE, FAKE, 17, None) != 0
     assert P.dsa_peak_copy(None, FAKE, 16, None) != 0
+
+
+def test_lds_poison_build_exports_the_same_entry_points():
+    # the debug build whose kernels poison their LDS first (compared with the
+    # product build in tests/test_gpu_lds_poison.py): built beside it by
+    # build(), the same C ABI and nothing else
+    from dsa_top_sparse_amd import build as hip_build
+    assert os.path.exists(hip_build.LDS_POISON_LIB), "run __graft_entry__.build() first"
+    nm = subprocess.run(["nm", "-D", "--defined-only", hip_build.LDS_POISON_LIB], capture_output=True, text=True,
+                        check=True).stdout
+    assert sorted(set(re.findall(r" T (dsa_[a-z0-9_]+)$", nm, flags=re.M))) == declared_functions()
+    assert not re.search(r" T _Z", nm)
+    with binding.use_library(hip_build.LDS_POISON_LIB) as P:
+        assert P._name == hip_build.LDS_POISON_LIB and binding.lib() is P
+        assert binding.status_string(SHAPE) != "unknown status"
+        d = dims(n_q=4, top_k=0)  # argument checks answer before any launch
+        assert P.dsa_sparse_mla_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None) == SHAPE
+    assert binding.lib()._name == binding.LIB_PATH
