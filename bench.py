@@ -338,6 +338,38 @@ def time_workload(torch, binding, cfg, dev, outs, stream, steps, warmup, flush, 
             "min": {k: min(v) for k, v in k_ms.items()}}
 
 
+def graph_replay(torch, binding, cfg, dev, outs, steps):
+    """The two-call step captured once into a HIP graph and replayed `steps`
+    times, as a serving loop would run it (the calls allocate nothing and
+    synchronise only on a device's first use). The last replay's indices and
+    outputs are compared with the eager step's. A capture that fails is
+    reported, not raised."""
+    try:
+        ref = {k: outs[k].clone() for k in ("idx", "out", "lse")}
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            binding.run_chunk(cfg, dev, outs)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            binding.run_chunk(cfg, dev, outs)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        same = all(torch.equal(ref[k], outs[k]) for k in ref)
+        del g
+        return {"ms_per_step": round(1e3 * wall / steps, 4), "query_tokens_per_s": round(cfg.n_q * steps / wall, 1),
+                "steps": steps, "same_as_eager": bool(same)}
+    except Exception as e:  # reported in the line; the eager figures stand
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def path_summary(torch, binding, cfg, dev, outs, stream, two_step, steps=10):
     """Both ways of running steps 1 and 2 on one workload: the two calls
     (scores in HBM) and the fused call (candidates only). `two_step` is a
@@ -439,6 +471,7 @@ def main():
     wall = timing["wall"]
     avg, med, mn = timing["avg"], timing["med"], timing["min"]
     ms_per_step = 1e3 * wall / args.steps
+    graph = graph_replay(torch, binding, cfg, dev, outs, args.steps) if (args.path == "two_step" and flush is None) else None
 
     w_idx, w_topk, w_attn = algorithmic_work(cfg)
     t_attn = avg["attention"] * 1e-3
@@ -510,6 +543,8 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
         "best_batch_ms_per_step": round(1e3 * best_batch, 4),
     }
+    if graph is not None:
+        line["graph_replay"] = graph
     if peaks is not None:
         line["measured_peaks"] = peaks
     if unions is not None:
