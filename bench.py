@@ -425,6 +425,7 @@ def main():
     ap.add_argument("--no-replay", dest="replay", action="store_false",
                     help="skip the side measurements: the other workloads, chunked-prefill replays of the pages' "
                          "prompts, and decode steps")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing (profiling runs)")
     ap.add_argument("--path", choices=("two_step", "fused"), default="two_step",
                     help="steps 1-2 as two calls (scores in HBM; the faster one on the 8k chunk at offset 8k) or as "
                          "the fused indexer + select")
@@ -471,7 +472,9 @@ def main():
     wall = timing["wall"]
     avg, med, mn = timing["avg"], timing["med"], timing["min"]
     ms_per_step = 1e3 * wall / args.steps
-    graph = graph_replay(torch, binding, cfg, dev, outs, args.steps) if (args.path == "two_step" and flush is None) else None
+    graph = None
+    if args.path == "two_step" and flush is None and not args.no_graph:
+        graph = graph_replay(torch, binding, cfg, dev, outs, args.steps)
 
     w_idx, w_topk, w_attn = algorithmic_work(cfg)
     t_attn = avg["attention"] * 1e-3
