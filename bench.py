@@ -513,14 +513,15 @@ def main():
             oinputs = synth.generate(ocfg)
             odev = binding.to_device(oinputs)
             oouts = binding.alloc_outputs(ocfg)
-            t = time_workload(torch, binding, ocfg, odev, oouts, stream, 10, 3, None)
+            n_side = 20
+            t = time_workload(torch, binding, ocfg, odev, oouts, stream, n_side, 10, None)
             if args.cpu_baseline_s > 0:
                 workloads_cpu[ocfg.name] = (ocfg, oinputs)
-            workloads[ocfg.name] = {"ms_per_step": round(1e3 * t["wall"] / 10, 4),
-                                    "query_tokens_per_s": round(ocfg.n_q * 10 / t["wall"], 1),
+            workloads[ocfg.name] = {"ms_per_step": round(1e3 * t["wall"] / n_side, 4),
+                                    "query_tokens_per_s": round(ocfg.n_q * n_side / t["wall"], 1),
                                     "kernels": kernel_summary(ocfg, t["avg"]),
                                     "paths": path_summary(torch, binding, ocfg, odev, oouts, stream,
-                                                          {"t": t, "steps": 10})}
+                                                          {"t": t, "steps": n_side})}
             del odev, oouts
             torch.cuda.empty_cache()
     replay = prefill_replay(torch, cfg, dev, stream) if args.replay else None
